@@ -1,0 +1,67 @@
+"""Strength of the oracle's pins: plant plausible mistakes in copies of the
+oracle's C source (built on the CPU with gcc into a temporary directory) and
+require that at least one pin fails for every planted mistake."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+# (description, exact text in tree_attn_oracle.c, replacement)
+MUTANTS = [
+    ("node does not see itself",
+     "for (int32_t j = i; j != -1; j = J->parent[off + j]) {\n        if (j < 0",
+     "for (int32_t j = J->parent[off + i]; j != -1; j = J->parent[off + j]) {\n        if (j < 0"),
+    ("siblings and other branches leak in",
+     "for (int32_t j = i; j != -1; j = J->parent[off + j]) {\n        if (j < 0",
+     "for (int32_t j = i; j != -1; j = (j > 0 ? j - 1 : -1)) {\n        if (j < 0"),
+    ("wrong GQA head map", "int32_t c = h / G;", "int32_t c = h % J->Hkv;"),
+    ("first prefix token dropped", "for (int32_t t = 0; t < L; ++t) {", "for (int32_t t = 1; t < L; ++t) {"),
+    ("wrong slot inside a page", "int64_t slot = (int64_t)page * J->page_size + t % J->page_size;",
+     "int64_t slot = (int64_t)page * J->page_size + (t + 1) % J->page_size;"),
+    ("LSE in base 2", "*lse = m + log(l);", "*lse = m + log2(l);"),
+    ("prefix scores unscaled", "score[n] = J->scale * dot(qrow, krow, D);\n        vrow[n] = J->v_cache",
+     "score[n] = dot(qrow, krow, D);\n        vrow[n] = J->v_cache"),
+    ("tree value of the wrong node", "vrow[n] = J->v_tree + ((int64_t)(off + j) * J->Hkv + c) * D;",
+     "vrow[n] = J->v_tree + ((int64_t)(off + i) * J->Hkv + c) * D;"),
+    ("max not subtracted in the weights", "double w = exp(score[k] - m) / l;", "double w = exp(score[k]) / l;"),
+    ("position id off by one", "pos_id[off + i] = prefix_len[b] + d - 1;", "pos_id[off + i] = prefix_len[b] + d;"),
+    ("mask bit shifted", "|= (uint64_t)1 << (j % 64);", "|= (uint64_t)1 << ((j + 1) % 64);"),
+    ("status index not one-based", "status[b] = first_bad + 1;", "status[b] = first_bad;"),
+    ("q row of the wrong head", "const double *qrow = J->q + ((int64_t)node * J->Hq + h) * D;",
+     "const double *qrow = J->q + ((int64_t)node * J->Hq + (h + 1) % J->Hq) * D;"),
+]
+
+PIN_CALLS = [
+    pins.test_plan_hand_fixture,
+    lambda: pins.test_plan_chain_closed_form(65),
+    pins.test_plan_recurrence_and_popcount,
+    pins.test_plan_error_statuses,
+    pins.test_attn_hand_fixture,
+    lambda: pins.test_chain_equals_causal_sdpa(45, 16, 16),
+    lambda: pins.test_path_as_flat_sequence(2, 4),
+    pins.test_zero_keys_closed_form,
+    pins.test_one_visible_key,
+    pins.test_non_ancestors_do_not_leak,
+]
+
+
+@pytest.mark.parametrize("desc,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(desc, old, new, tmp_path, monkeypatch):
+    src = open(oracle._SRC).read()
+    assert src.count(old) == 1, f"mutation site not unique/present: {desc}"
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-w", "-o", str(so),
+                           str(mpath), "-lm", "-lpthread"])
+    monkeypatch.setattr(oracle, "_lib", oracle.load_library(str(so)))
+    caught = 0
+    for call in PIN_CALLS:
+        try:
+            call()
+        except (AssertionError, ValueError):
+            caught += 1
+    assert caught > 0, f"no pin caught the planted mistake: {desc}"
