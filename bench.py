@@ -1,0 +1,382 @@
+#!/usr/bin/env python3
+"""Throughput of tree-causal paged attention on one MI355X.
+
+One *step* is the whole hot path of one decode step over one batch of
+synthetic inputs: ``tree_attn_plan`` (parent array -> ancestor bitmask,
+depth, position ids) followed by ``tree_attn_fwd`` (its attention kernel and,
+when the prefix is split, the split-K merge).  Inputs are resident in HBM
+before timing starts; the step is replayed from HIP graphs so that the
+microsecond-scale launches are not limited by the Python launch rate, and
+successive steps rotate over enough input replicas that the working set does
+not stay in the 256 MB Infinity Cache.
+
+Default workload: ``chain16`` (budget 16: 1 request, prefix 2048, a 16-node
+chain, 32/8 heads, head_dim 128, bf16), the HBM-bound case.  The same run also
+measures ``moe`` (budget 256: 32 requests, prefix 4096, best-first trees of
+256 nodes, 32/4 heads), the MFMA-bound case, and reports it under
+``budget256``.  One JSON line goes to stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+import tree_masked_attention_plan_amd as ta  # noqa: E402
+from tree_masked_attention_plan_amd import workloads as W  # noqa: E402
+
+METRIC = "tree-attn tree tokens/s + % bf16 MFMA peak (budget 256) / % HBM BW (budget 16)"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_FP32_TFLOPS = 157.3
+KERNEL_SRC = os.path.join(HERE, "tree_masked_attention_plan_amd", "csrc", "kernels.hip")
+PROFILES = os.path.join(HERE, "profiles")
+ROTATE_BYTES = 600 << 20       # cycle at least this much input per pass over replicas
+MAX_REPLICAS = 64
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- accounting
+
+def node_depths(w: W.Workload) -> np.ndarray:
+    """Path length of every node (host-side statistic for work accounting)."""
+    par = w.parent.numpy()
+    off = w.tree_off.numpy()
+    d = np.zeros(w.N, dtype=np.int64)
+    for b in range(w.B):
+        for i in range(off[b + 1] - off[b]):
+            p = par[off[b] + i]
+            d[off[b] + i] = 1 if p < 0 else d[off[b] + p] + 1
+    return d
+
+
+def work(w: W.Workload, nsplit: int) -> dict:
+    """Algorithmic work of one forward call, over visible (query, key) pairs.
+
+    flops = 4 * D * Hq * (sum_b T_b * L_b + sum_i depth_i)   (QK^T and PV)
+    bytes = valid prefix K/V + tree K/V + Q + O + LSE + mask words that can
+            hold a visible bit (ceil(T_b / 64) per node) + live block-table
+            entries.  ``kernel_bytes`` is the part the attention kernel itself
+            must move: everything but O and LSE when a separate merge writes
+            them (split count > 1)."""
+    e = torch.tensor([], dtype=w.dtype).element_size()
+    T = w.tree_sizes
+    L = w.prefix_len.numpy().astype(np.int64)
+    sdepth = int(node_depths(w).sum())
+    pairs = int((T * L).sum()) + sdepth
+    flops = 4.0 * w.D * w.Hq * pairs
+    N = w.N
+    kv = int(L.sum()) * w.Hkv * w.D * 2 * e + N * w.Hkv * w.D * 2 * e
+    q = N * w.Hq * w.D * e
+    o = N * w.Hq * w.D * e + N * w.Hq * 4
+    mask = int((T * ((T + 63) // 64)).sum()) * 8
+    bt = int(((L + w.page_size - 1) // w.page_size).sum()) * 4
+    total = kv + q + o + mask + bt
+    kernel = total if nsplit == 1 else total - o
+    return {"flops": flops, "bytes": float(total), "kernel_bytes": float(kernel),
+            "pairs": pairs, "sum_depth": sdepth, "tree_tokens": N}
+
+
+# ---------------------------------------------------------------- device side
+
+class Replica:
+    def __init__(self, w: W.Workload, dev):
+        self.w = w.to(dev)
+        n, b = w.N, w.B
+        self.plan_out = ta.PlanResult(torch.empty((n, ta.MASK_WORDS), dtype=torch.int64, device=dev),
+                                      torch.empty(n, dtype=torch.int32, device=dev),
+                                      torch.empty(n, dtype=torch.int32, device=dev),
+                                      torch.empty(b, dtype=torch.int32, device=dev))
+        # the plan writes anc_mask before the forward reads it; run it once
+        # here so that the forward can be prepared against the same buffers
+        ta.plan(self.w.parent, self.w.tree_off, self.w.prefix_len, max_tree=w.max_tree,
+                out=self.plan_out)
+        self.call = ta.prepare_fwd(self.w.q, self.w.k_tree, self.w.v_tree, self.w.k_cache,
+                                   self.w.v_cache, self.w.block_table, self.w.prefix_len,
+                                   self.w.tree_off, self.plan_out.anc_mask, max_tree=w.max_tree,
+                                   max_prefix=w.max_prefix)
+        self.max_tree = w.max_tree
+
+    def step(self):
+        ta.plan(self.w.parent, self.w.tree_off, self.w.prefix_len, max_tree=self.max_tree,
+                out=self.plan_out)
+        self.call.partial()
+        self.call.merge()
+
+    def partial(self):
+        self.call.partial()
+
+
+def replica_bytes(w: W.Workload) -> int:
+    t = 0
+    for x in (w.q, w.k_tree, w.v_tree, w.k_cache, w.v_cache):
+        t += x.numel() * x.element_size()
+    return t
+
+
+def capture(fn, n_rep):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n_rep):
+            fn()
+    return g
+
+
+class Runner:
+    """Graphs over the replicas: ``chunk`` runs one step on every replica in
+    turn, ``single[r]`` one step on replica r, ``partial_chunk`` only the
+    attention kernel on every replica (for the per-launch kernel time)."""
+
+    def __init__(self, reps):
+        self.reps = reps
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for r in reps:        # eager warm-up before capture
+                r.step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.chunk = capture(lambda: [r.step() for r in reps], 1)
+        self.single = [capture(r.step, 1) for r in reps]
+        self.partial_chunk = capture(lambda: [r.partial() for r in reps], 1)
+        torch.cuda.synchronize()
+
+    def run_steps(self, k):
+        R = len(self.reps)
+        for _ in range(k // R):
+            self.chunk.replay()
+        for i in range(k % R):
+            self.single[i].replay()
+
+
+def time_steps(runner: Runner, steps: int, warmup: int) -> float:
+    runner.run_steps(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    runner.run_steps(steps)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def time_partial_kernel(runner: Runner, min_launches: int = 200) -> float:
+    """Average duration (s) of one attention-kernel launch: HIP events on the
+    stream the graph's kernels run on, around back-to-back replays."""
+    R = len(runner.reps)
+    reps = max(1, math.ceil(min_launches / R))
+    runner.partial_chunk.replay()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        runner.partial_chunk.replay()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / (reps * R)
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(w: W.Workload, target_s: float) -> dict:
+    """The fp64 oracle on this host, on a bounded sample of the workload.
+
+    Inputs are widened to fp64 once, outside the timed calls; the oracle runs
+    with one thread per available core."""
+    import oracle
+    threads = oracle.default_threads()
+    arrays = [x.double().numpy() for x in (w.q, w.k_tree, w.v_tree, w.k_cache, w.v_cache)]
+    ints = [x.numpy() for x in (w.block_table, w.prefix_len, w.tree_off, w.parent)]
+
+    def run(rows=None):
+        return oracle.tree_attn(*arrays, *ints, scale=w.scale, rows=rows, threads=threads)
+
+    rows_total = w.N * w.Hq
+    # estimate the cost per row from a small slice, then size the sample
+    probe = np.arange(0, rows_total, max(1, rows_total // 256), dtype=np.int64)[:256]
+    t0 = time.perf_counter()
+    run(probe)
+    per_row = max((time.perf_counter() - t0) / len(probe), 1e-9)
+    if per_row * rows_total <= target_s:
+        reps = max(1, int(target_s / (per_row * rows_total)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            run()
+        dt = time.perf_counter() - t0
+        tokens = w.N * reps
+        sample = f"the whole workload ({w.N} tree tokens, {rows_total} rows), {reps} runs"
+    else:
+        n_nodes = max(1, min(w.N, int(target_s / per_row) // w.Hq))
+        nodes = np.sort(np.random.default_rng(0).choice(w.N, size=n_nodes, replace=False))
+        rows = (nodes[:, None] * w.Hq + np.arange(w.Hq)[None, :]).reshape(-1)
+        t0 = time.perf_counter()
+        run(rows)
+        dt = time.perf_counter() - t0
+        tokens = n_nodes
+        sample = (f"{n_nodes} of {w.N} tree tokens (all {w.Hq} heads each), seeded uniform "
+                  f"sample, 1 run")
+    return {"value": tokens / dt, "unit": "tree tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+# ---------------------------------------------------------------- traffic
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch of the attention kernel from committed counter
+    summaries, or None if absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"fwd_bf16_kernel_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        t = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_src_sha256_16") != kernel_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- main
+
+def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: float) -> dict:
+    w = W.make_config(name)
+    per = replica_bytes(w)
+    R = max(1, min(MAX_REPLICAS, math.ceil(ROTATE_BYTES / per)))
+    log(f"[bench] {name}: B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} D={w.D} max_prefix={w.max_prefix} "
+        f"replicas={R} ({per / 2**20:.1f} MiB each)")
+    reps = [Replica(w, dev) for _ in range(R)]
+    ta.check_status(reps[0].plan_out.status)
+    runner = Runner(reps)
+    nsplit = reps[0].call.num_splits
+    wk = work(w, nsplit)
+    dt = time_steps(runner, steps, warmup)
+    ms = dt / steps * 1e3
+    t_kern = time_partial_kernel(runner)
+    log(f"[bench] {name}: {ms * 1e3:.2f} us/step, attention kernel {t_kern * 1e6:.2f} us/launch, "
+        f"splits={nsplit}")
+    res = {
+        "workload": name,
+        "value": wk["tree_tokens"] * steps / dt,
+        "ms_per_step": ms,
+        "num_splits": nsplit,
+        "tflops_step": wk["flops"] / (ms * 1e-3) / 1e12,
+        "kernel_us": t_kern * 1e6,
+        "work": wk,
+        "config": {"workload": name, "B": w.B, "tree_tokens": w.N, "max_tree": w.max_tree,
+                   "prefix_tokens": int(w.prefix_len.sum()), "max_prefix": w.max_prefix,
+                   "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D, "page_size": w.page_size,
+                   "num_splits": nsplit, "replicas": R},
+    }
+    is_bf16 = w.dtype == torch.bfloat16
+    if name == "moe" or name == "tree256" or name == "mixed":
+        ach = wk["flops"] / t_kern / 1e12
+        peak = PEAK_BF16_TFLOPS if is_bf16 else PEAK_FP32_TFLOPS
+        res["roofline"] = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                           "frac": ach / peak, "traffic": traffic_for(name),
+                           "kernel": "fwd_bf16_kernel", "kernel_us": t_kern * 1e6}
+    else:
+        ach = wk["kernel_bytes"] / t_kern / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": ach / PEAK_HBM_GBS, "traffic": traffic_for(name),
+                           "kernel": "fwd_bf16_kernel" if is_bf16 else "fwd_f32_kernel",
+                           "kernel_us": t_kern * 1e6}
+    del runner, reps
+    torch.cuda.empty_cache()
+    if cpu:
+        res["cpu_baseline"] = cpu_baseline(w, cpu_seconds)
+        log(f"[bench] {name}: oracle {res['cpu_baseline']['value']:.1f} tree tokens/s on "
+            f"{res['cpu_baseline']['cores']} cores ({res['cpu_baseline']['sample']})")
+    return res
+
+
+def calibrate_copy(mib: int, reps: int):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    dev = torch.device("cuda:0")
+    n = (mib << 20) // 4
+    a = torch.randn(n, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        torch.add(a, 0.0, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="chain16", choices=[n for n in W.CONFIG_NAMES])
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the budget-256 (moe) measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain copy kernel of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(this path shards by request or kv head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib, 10)
+        return
+    ta.load_library()
+    dev = torch.device("cuda:0")
+    cpu = not args.no_cpu_baseline
+    main_res = measure(args.workload, args.steps, args.warmup, dev, cpu, args.cpu_seconds)
+    w_dtype = "f32" if args.workload == "tiny" else "bf16"
+    line = {
+        "metric": METRIC,
+        "value": main_res["value"],
+        "unit": "tree tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w_dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V, shuffled page pool, synthetic trees)",
+        "config": main_res["config"],
+        "roofline": main_res["roofline"],
+    }
+    if "cpu_baseline" in main_res:
+        line["cpu_baseline"] = main_res["cpu_baseline"]
+    line["tflops"] = main_res["tflops_step"]
+    if not args.no_secondary and args.workload != "moe":
+        sec = measure("moe", max(20, args.steps // 10), max(2, args.warmup // 10), dev, cpu,
+                      args.cpu_seconds)
+        line["budget256"] = {"workload": "moe", "value": sec["value"], "unit": "tree tokens/s",
+                             "ms_per_step": sec["ms_per_step"], "steps": max(20, args.steps // 10),
+                             "tflops": sec["tflops_step"], "config": sec["config"],
+                             "roofline": sec["roofline"]}
+        if "cpu_baseline" in sec:
+            line["budget256"]["cpu_baseline"] = sec["cpu_baseline"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,230 @@
+/*
+ * tree_attn.h -- C ABI of the tree-causal paged attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (JetFlow: Breaking the Scaling Ceiling of Speculative
+ * Decoding with Parallel Tree Drafting -- technical summary, section 2, core
+ * architecture, "tree-causal attention mask", and the branch factorisation
+ * equation in the same paragraph): every node of a drafted token tree attends
+ * to the original input prefix and to its in-tree ancestors, itself included,
+ * and never to its descendants or to unrelated sibling branches.  The same
+ * operation serves the causal parallel draft head and target-model tree
+ * verification, where the prefix lives in a paged KV cache (section 3,
+ * "industrial integration": a paged FlashAttention with tree-mask staging).
+ *
+ * Two device entry points make up one decode step's attention:
+ *   tree_attn_plan  parent array  -> ancestor bitmask, depth, position ids
+ *   tree_attn_fwd   GQA attention over the paged prefix plus the tree's own
+ *                   K/V under the ancestor bitmask; online softmax; fp32 LSE
+ *
+ * Conventions shared by every call:
+ *  - All device buffers are allocated and owned by the caller; the library
+ *    allocates nothing and keeps no state.  Calls are reentrant.
+ *  - Pointers marked (device) are device memory on the current HIP device;
+ *    (host) pointers are host memory.  Every layout is row-major, contiguous.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Device
+ *    work is enqueued on it and the call returns without synchronising.
+ *  - Errors the host can see (null pointers, bad sizes, unsupported
+ *    configurations, a short workspace) are returned synchronously before
+ *    anything is launched.  TA_ERR_HIP reports a failed launch.  Outputs are
+ *    undefined after any error.
+ *  - Requests are numbered b = 0..B-1; request b owns tree nodes
+ *    tree_off[b] .. tree_off[b+1]-1 (global node ids, cu_seqlens style).
+ *    Inside a request nodes use local ids 0..T_b-1, T_b = tree_off[b+1] -
+ *    tree_off[b], in topological order: parent[i] < i, and parent[i] = -1
+ *    means node i hangs directly off the prefix (a forest is allowed).
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TREE_ATTN_ABI_VERSION 1
+/* u64 words per node row of the ancestor bitmask (fixed, so plan and fwd can
+ * never disagree on the layout); bit j of word w is local node 64*w + j. */
+#define TREE_ATTN_MASK_WORDS 4
+/* largest tree a request may have: 64 * TREE_ATTN_MASK_WORDS */
+#define TREE_ATTN_MAX_TREE 256
+
+typedef enum {
+    TA_OK = 0,
+    TA_ERR_NULL_PTR = 1,    /* a required pointer is NULL                    */
+    TA_ERR_BAD_SHAPE = 2,   /* inconsistent or out-of-range sizes            */
+    TA_ERR_UNSUPPORTED = 3, /* valid but not implemented (dtype, head_dim..) */
+    TA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required    */
+    TA_ERR_HIP = 5          /* a HIP launch failed                           */
+} ta_status_t;
+
+typedef enum {
+    TA_DTYPE_BF16 = 0, /* bf16 Q/K/V/O, fp32 accumulation, bf16 MFMA          */
+    TA_DTYPE_FP32 = 1  /* fp32 Q/K/V/O, fp32 arithmetic throughout            */
+} ta_dtype_t;
+
+/* Per-request codes that tree_attn_plan writes into status[b]. */
+#define TA_TREE_OK 0
+#define TA_TREE_BAD_OFFSETS (-1) /* tree_off[0] != 0, tree_off[B] != N, a
+                                    negative tree size, or T_b > max_tree   */
+#define TA_TREE_BAD_PREFIX (-2)  /* prefix_len[b] < 0                       */
+/* status[b] = k > 0: local node k-1 is the first node whose parent is not in
+ * [-1, k-2] (not topologically ordered).  Codes are checked in the order
+ * offsets, prefix, parents; the first failing check is reported. */
+
+/* ABI version of the loaded library (TREE_ATTN_ABI_VERSION). */
+int tree_attn_abi_version(void);
+
+/* Static description of a ta_status_t value; never NULL. */
+const char *tree_attn_status_str(int status);
+
+/*
+ * tree_attn_plan -- the ancestor sets of every tree node.
+ *
+ * For local node i of request b, A(i) = {i} U A(parent[i]) with A(-1) empty:
+ * the node's root path, itself included (the set of tree keys the node sees,
+ * per the mask definition above).
+ *   anc_mask[n, w] (device, u64 [N, TREE_ATTN_MASK_WORDS]): bit j of word w is
+ *                  set iff local node 64*w + j is in A(i), n = tree_off[b]+i.
+ *   depth[n]       (device, i32 [N]): |A(i)| (>= 1).
+ *   pos_id[n]      (device, i32 [N]): prefix_len[b] + depth[n] - 1, the
+ *                  node's position in the flat sequence prefix ++ root path
+ *                  (for rotary embeddings).
+ *   status[b]      (device, i32 [B]): TA_TREE_OK or a TA_TREE_* code / k > 0
+ *                  as described above.  Rows of a request with a non-zero
+ *                  status are left unwritten.  Read it after synchronising.
+ * Inputs (device): parent [N] i32 local ids, tree_off [B+1] i32,
+ * prefix_len [B] i32.  max_tree (host) bounds every T_b, 0..256.
+ * B = 0 or N = 0 is a valid no-op (status is still written for every b).
+ */
+ta_status_t tree_attn_plan(const int32_t *parent, const int32_t *tree_off,
+                           const int32_t *prefix_len, int32_t B, int32_t N,
+                           int32_t max_tree, uint64_t *anc_mask, int32_t *depth,
+                           int32_t *pos_id, int32_t *status, void *stream);
+
+/*
+ * Number of prefix splits (split-K over the paged prefix, merged by LSE) that
+ * tree_attn_fwd uses for these sizes when num_splits = 0 is passed; a pure
+ * function of its arguments.  Returns 0 for invalid sizes.
+ */
+int32_t tree_attn_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                             int32_t max_tree, int32_t max_prefix, ta_dtype_t dtype);
+
+/*
+ * Workspace bytes tree_attn_fwd needs for these sizes and this split count
+ * (num_splits = 0: the automatic choice).  0 when no workspace is needed.
+ * A pure function of its arguments.
+ */
+size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                                 int32_t D, int32_t max_tree, int32_t max_prefix,
+                                 ta_dtype_t dtype, int32_t num_splits);
+
+/*
+ * tree_attn_fwd -- tree-causal attention of every (node, q-head) row.
+ *
+ * Row (n, h), n = tree_off[b] + i, kv head c = h / (Hq / Hkv) (contiguous
+ * GQA groups), sees
+ *   the prefix:  K_t = k_cache[block_table[b, t / page_size], t % page_size, c]
+ *                for 0 <= t < prefix_len[b]   (V likewise), and
+ *   the tree:    K_j = k_tree[tree_off[b] + j, c] for every j in A(i)
+ *                (bits of anc_mask[n]; V likewise),
+ * with s = softmax_scale * <q[n,h], K>,
+ *   out[n,h] = sum softmax(s) V    (in the input dtype),
+ *   lse[n,h] = ln sum exp(s)       (fp32, natural log).
+ *
+ * Buffers (device):
+ *   q           [N, Hq, D]                         dtype
+ *   k_tree      [N, Hkv, D], v_tree likewise       dtype
+ *   k_cache     [num_pages, page_size, Hkv, D]     dtype (separate K and V pools)
+ *   v_cache     likewise
+ *   block_table [B, max_pages_per_seq] i32 physical page ids; entries past
+ *               ceil(prefix_len[b] / page_size) are never read
+ *   prefix_len  [B] i32,  tree_off [B+1] i32
+ *   anc_mask    [N, TREE_ATTN_MASK_WORDS] u64, as written by tree_attn_plan
+ *   out         [N, Hq, D] dtype;  lse [N, Hq] f32
+ *   workspace   tree_attn_workspace_bytes(...) bytes, 256-byte aligned, or
+ *               NULL when that is 0; its contents are scratch between calls
+ * Host sizes: max_tree >= every T_b (<= 256), max_prefix >= every
+ *   prefix_len[b] (<= max_pages_per_seq * page_size).  They size the launch
+ *   so no call ever reads device data on the host.
+ * softmax_scale <= 0 selects 1/sqrt(D).  num_splits = 0 selects
+ *   tree_attn_num_splits(...); 1..64 forces a split count.
+ * Supported: dtype bf16 or fp32; D in {64, 128}; page_size a power of two in
+ *   [1, 1024]; Hq % Hkv == 0.  Anything else is TA_ERR_UNSUPPORTED or
+ *   TA_ERR_BAD_SHAPE.
+ * Device-side robustness: a page id outside [0, num_pages) or a prefix
+ *   longer than the block table makes the kernel skip those keys rather than
+ *   read outside the pool; tree sizes above max_tree are clamped.  Such inputs
+ *   are caller errors and give undefined (but memory-safe) results.
+ */
+ta_status_t tree_attn_fwd(const void *q, const void *k_tree, const void *v_tree,
+                          const void *k_cache, const void *v_cache,
+                          const int32_t *block_table, const int32_t *prefix_len,
+                          const int32_t *tree_off, const uint64_t *anc_mask,
+                          int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                          int32_t page_size, int32_t num_pages,
+                          int32_t max_pages_per_seq, int32_t max_tree,
+                          int32_t max_prefix, float softmax_scale, ta_dtype_t dtype,
+                          int32_t num_splits, void *out, float *lse, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
+ * The two stages of tree_attn_fwd, for callers that schedule or time them
+ * separately.  Both take exactly the arguments of tree_attn_fwd and run the
+ * same host checks; tree_attn_fwd is tree_attn_fwd_partial followed by
+ * tree_attn_merge on the same stream.
+ *   tree_attn_fwd_partial  launches the attention kernel.  With one prefix
+ *                          split it writes out / lse itself; otherwise each
+ *                          split writes its normalised partial output and its
+ *                          partial log-sum-exp into the workspace.
+ *   tree_attn_merge        combines the splits' partials into out / lse by
+ *                          the log-sum-exp rule (split-K merge); a no-op
+ *                          when there is one split.  It must follow the
+ *                          partial stage of the same call, with the same
+ *                          arguments and the workspace untouched.
+ */
+ta_status_t tree_attn_fwd_partial(const void *q, const void *k_tree, const void *v_tree,
+                                  const void *k_cache, const void *v_cache,
+                                  const int32_t *block_table, const int32_t *prefix_len,
+                                  const int32_t *tree_off, const uint64_t *anc_mask,
+                                  int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t page_size, int32_t num_pages,
+                                  int32_t max_pages_per_seq, int32_t max_tree,
+                                  int32_t max_prefix, float softmax_scale, ta_dtype_t dtype,
+                                  int32_t num_splits, void *out, float *lse, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+ta_status_t tree_attn_merge(const void *q, const void *k_tree, const void *v_tree,
+                            const void *k_cache, const void *v_cache,
+                            const int32_t *block_table, const int32_t *prefix_len,
+                            const int32_t *tree_off, const uint64_t *anc_mask,
+                            int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                            int32_t page_size, int32_t num_pages,
+                            int32_t max_pages_per_seq, int32_t max_tree,
+                            int32_t max_prefix, float softmax_scale, ta_dtype_t dtype,
+                            int32_t num_splits, void *out, float *lse, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * The host-side argument check of tree_attn_fwd, on its own: returns exactly
+ * what tree_attn_fwd would return before launching anything (TA_OK if it
+ * would launch).  Launches nothing and touches no device memory.
+ */
+ta_status_t tree_attn_fwd_check(const void *q, const void *k_tree, const void *v_tree,
+                                const void *k_cache, const void *v_cache,
+                                const int32_t *block_table, const int32_t *prefix_len,
+                                const int32_t *tree_off, const uint64_t *anc_mask,
+                                int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                int32_t page_size, int32_t num_pages,
+                                int32_t max_pages_per_seq, int32_t max_tree,
+                                int32_t max_prefix, float softmax_scale, ta_dtype_t dtype,
+                                int32_t num_splits, const void *out, const float *lse,
+                                const void *workspace, size_t workspace_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H */

@@ -1,0 +1,19 @@
+"""Tree-causal paged attention for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libtree_attn.so`` (C ABI in ``include/tree_attn.h``).
+It only marshals arguments: torch tensors supply device memory and the
+current HIP stream, every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library is not built, importing the
+binding's entry points raises.
+
+    plan(parent, tree_off, prefix_len)   -> anc_mask, depth, pos_id, status
+    fwd(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
+        tree_off, anc_mask)               -> out, lse
+"""
+from ._binding import (MASK_WORDS, MAX_TREE, FwdCall, PlanResult, TreeAttnError, abi_version,
+                       check_status, fwd, library_path, load_library, num_splits, plan, prepare_fwd,
+                       workspace_bytes)
+
+__all__ = ["MASK_WORDS", "MAX_TREE", "FwdCall", "PlanResult", "TreeAttnError", "abi_version",
+           "check_status", "fwd", "library_path", "load_library", "num_splits", "plan",
+           "prepare_fwd", "workspace_bytes"]

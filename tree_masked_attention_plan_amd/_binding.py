@@ -1,0 +1,289 @@
+"""ctypes marshalling for libtree_attn.so; see include/tree_attn.h for the
+contract of every call (layouts, ownership, error codes)."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import NamedTuple, Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libtree_attn.so"
+
+MASK_WORDS = 4
+MAX_TREE = 256
+TA_DTYPE = {torch.bfloat16: 0, torch.float32: 1}
+
+_lib = None
+
+
+class TreeAttnError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load the in-tree HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build the HIP library first "
+                          f"(python -m tree_masked_attention_plan_amd.build)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    lib.tree_attn_abi_version.restype = ctypes.c_int
+    lib.tree_attn_abi_version.argtypes = []
+    lib.tree_attn_status_str.restype = ctypes.c_char_p
+    lib.tree_attn_status_str.argtypes = [ctypes.c_int]
+    lib.tree_attn_plan.restype = ctypes.c_int
+    lib.tree_attn_plan.argtypes = [P, P, P, i32, i32, i32, P, P, P, P, P]
+    lib.tree_attn_num_splits.restype = i32
+    lib.tree_attn_num_splits.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.tree_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.tree_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
+    fwd_args = [P, P, P, P, P, P, P, P, P,
+                i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                ctypes.c_float, ctypes.c_int, i32, P, P, P, ctypes.c_size_t]
+    for name in ("tree_attn_fwd", "tree_attn_fwd_partial", "tree_attn_merge"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = fwd_args + [P]
+    lib.tree_attn_fwd_check.restype = ctypes.c_int
+    lib.tree_attn_fwd_check.argtypes = fwd_args
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load_library().tree_attn_abi_version()
+
+
+def _raise(rc: int, what: str):
+    if rc != 0:
+        msg = load_library().tree_attn_status_str(rc).decode()
+        raise TreeAttnError(f"{what}: {msg} (status {rc})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_tensor(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+class PlanResult(NamedTuple):
+    anc_mask: torch.Tensor   # [N, 4] int64 bit patterns of u64 words
+    depth: torch.Tensor      # [N] int32
+    pos_id: torch.Tensor     # [N] int32
+    status: torch.Tensor     # [B] int32
+
+
+def _max_tree_of(tree_off: torch.Tensor) -> int:
+    if tree_off.numel() <= 1:
+        return 0
+    return int((tree_off[1:] - tree_off[:-1]).max().item())   # synchronises
+
+
+def plan(parent: torch.Tensor, tree_off: torch.Tensor, prefix_len: torch.Tensor,
+         max_tree: Optional[int] = None, *, out: Optional[PlanResult] = None,
+         stream=None) -> PlanResult:
+    """Ancestor bitmask, depth and position ids of every tree node.
+
+    ``max_tree`` (a host bound on every tree size) avoids a device sync when
+    given.  ``status`` is written on the device; :func:`check_status` reads it.
+    """
+    _dev_tensor(parent, "parent", torch.int32)
+    _dev_tensor(tree_off, "tree_off", torch.int32)
+    _dev_tensor(prefix_len, "prefix_len", torch.int32)
+    dev = parent.device
+    B = prefix_len.numel()
+    N = parent.numel()
+    if tree_off.numel() != B + 1:
+        raise ValueError("tree_off must have B+1 entries")
+    if max_tree is None:
+        max_tree = _max_tree_of(tree_off)
+    if out is None:
+        out = PlanResult(torch.empty((N, MASK_WORDS), dtype=torch.int64, device=dev),
+                         torch.empty(N, dtype=torch.int32, device=dev),
+                         torch.empty(N, dtype=torch.int32, device=dev),
+                         torch.empty(B, dtype=torch.int32, device=dev))
+    rc = load_library().tree_attn_plan(_ptr(parent), _ptr(tree_off), _ptr(prefix_len), B, N,
+                                       int(max_tree), _ptr(out.anc_mask), _ptr(out.depth),
+                                       _ptr(out.pos_id), _ptr(out.status), _stream(dev, stream))
+    _raise(rc, "tree_attn_plan")
+    return out
+
+
+def check_status(status: torch.Tensor) -> None:
+    """Raise if any request's plan status is non-zero (synchronises)."""
+    s = status.cpu()
+    bad = torch.nonzero(s).flatten().tolist()
+    if bad:
+        b = bad[0]
+        code = int(s[b])
+        if code == -1:
+            why = "inconsistent tree offsets or a tree larger than max_tree"
+        elif code == -2:
+            why = "negative prefix length"
+        else:
+            why = f"node {code - 1} has a parent that does not precede it"
+        raise TreeAttnError(f"request {b}: {why} (status {code}); bad requests: {bad}")
+
+
+def num_splits(B: int, Hq: int, Hkv: int, D: int, max_tree: int, max_prefix: int,
+               dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(load_library().tree_attn_num_splits(B, Hq, Hkv, D, max_tree, max_prefix, TA_DTYPE[dtype]))
+
+
+def workspace_bytes(B: int, N: int, Hq: int, Hkv: int, D: int, max_tree: int, max_prefix: int,
+                    dtype: torch.dtype = torch.bfloat16, num_splits: int = 0) -> int:
+    return int(load_library().tree_attn_workspace_bytes(B, N, Hq, Hkv, D, max_tree, max_prefix,
+                                                        TA_DTYPE[dtype], num_splits))
+
+
+class FwdCall:
+    """One forward call with its arguments marshalled once.
+
+    ``run()`` enqueues the whole operation, ``partial()`` / ``merge()`` its two
+    stages (see tree_attn_fwd_partial / tree_attn_merge); all on ``stream``
+    (default: the current stream at call time).  ``out`` / ``lse`` hold the
+    results once the stream reaches that point.
+    """
+
+    def __init__(self, args, out, lse, workspace, nsplit):
+        self._args = args
+        self.out = out
+        self.lse = lse
+        self.workspace = workspace
+        self.num_splits = nsplit
+        self._lib = load_library()
+
+    def _call(self, fn, name, stream):
+        rc = fn(*self._args, _stream(self.out.device, stream))
+        _raise(rc, name)
+        return self
+
+    def run(self, stream=None):
+        return self._call(self._lib.tree_attn_fwd, "tree_attn_fwd", stream)
+
+    def partial(self, stream=None):
+        return self._call(self._lib.tree_attn_fwd_partial, "tree_attn_fwd_partial", stream)
+
+    def merge(self, stream=None):
+        return self._call(self._lib.tree_attn_merge, "tree_attn_merge", stream)
+
+
+def prepare_fwd(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, k_cache: torch.Tensor,
+                v_cache: torch.Tensor, block_table: torch.Tensor, prefix_len: torch.Tensor,
+                tree_off: torch.Tensor, anc_mask: torch.Tensor, *, max_tree: Optional[int] = None,
+                max_prefix: Optional[int] = None, scale: Optional[float] = None, num_splits: int = 0,
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> FwdCall:
+    """Check and marshal the arguments of a forward call; see :func:`fwd`."""
+    if q.dtype not in TA_DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dt = q.dtype
+    for name, t in (("q", q), ("k_tree", k_tree), ("v_tree", v_tree), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        _dev_tensor(t, name, dt)
+    _dev_tensor(block_table, "block_table", torch.int32)
+    _dev_tensor(prefix_len, "prefix_len", torch.int32)
+    _dev_tensor(tree_off, "tree_off", torch.int32)
+    _dev_tensor(anc_mask, "anc_mask", torch.int64)
+    if q.dim() != 3 or k_tree.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q/k_tree must be [N,H,D] and k_cache [pages,page_size,Hkv,D]")
+    N, Hq, D = q.shape
+    Hkv = k_tree.shape[1]
+    if k_tree.shape != (N, Hkv, D) or v_tree.shape != k_tree.shape:
+        raise ValueError("k_tree/v_tree must be [N,Hkv,D]")
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    if k_cache.shape[2:] != (Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [num_pages,page_size,Hkv,D]")
+    B = prefix_len.numel()
+    if tree_off.numel() != B + 1 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("tree_off must be [B+1] and block_table [B, max_pages]")
+    if anc_mask.shape != (N, MASK_WORDS):
+        raise ValueError(f"anc_mask must be [N,{MASK_WORDS}]")
+    max_pages = block_table.shape[1]
+    dev = q.device
+    if max_tree is None:
+        max_tree = _max_tree_of(tree_off)
+    if max_prefix is None:
+        max_prefix = int(prefix_len.max().item()) if B else 0
+    if out is None:
+        out = torch.empty((N, Hq, D), dtype=dt, device=dev)
+    else:
+        _dev_tensor(out, "out", dt)
+        if out.shape != (N, Hq, D):
+            raise ValueError("out must be [N,Hq,D]")
+    if lse is None:
+        lse = torch.empty((N, Hq), dtype=torch.float32, device=dev)
+    else:
+        _dev_tensor(lse, "lse", torch.float32)
+        if lse.shape != (N, Hq):
+            raise ValueError("lse must be [N,Hq]")
+    lib = load_library()
+    need = lib.tree_attn_workspace_bytes(B, N, Hq, Hkv, D, max_tree, max_prefix, TA_DTYPE[dt], num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _dev_tensor(workspace, "workspace", torch.uint8)
+        base = workspace.data_ptr()
+        pad = (-base) % 256
+        ws_ptr = ctypes.c_void_p(base + pad)
+        ws_bytes = max(0, workspace.numel() - pad)
+    sc = 0.0 if scale is None else float(scale)
+    if not math.isfinite(sc):
+        raise ValueError("scale must be finite")
+    args = (_ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(prefix_len), _ptr(tree_off), _ptr(anc_mask), B, N, Hq, Hkv, D, page_size, num_pages,
+            max_pages, int(max_tree), int(max_prefix), sc, TA_DTYPE[dt], int(num_splits), _ptr(out),
+            _ptr(lse), ws_ptr, ws_bytes)
+    rc = lib.tree_attn_fwd_check(*args)
+    _raise(rc, "tree_attn_fwd")
+    nsplit = lib.tree_attn_num_splits(B, Hq, Hkv, D, int(max_tree), int(max_prefix), TA_DTYPE[dt]) \
+        if num_splits == 0 else num_splits
+    return FwdCall(args, out, lse, workspace, nsplit)
+
+
+def fwd(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, k_cache: torch.Tensor,
+        v_cache: torch.Tensor, block_table: torch.Tensor, prefix_len: torch.Tensor,
+        tree_off: torch.Tensor, anc_mask: torch.Tensor, *, max_tree: Optional[int] = None,
+        max_prefix: Optional[int] = None, scale: Optional[float] = None, num_splits: int = 0,
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None, stream=None):
+    """Tree-causal attention; returns ``(out [N,Hq,D], lse [N,Hq] fp32)``.
+
+    ``max_tree`` / ``max_prefix`` are host bounds; when omitted they are read
+    from the device (a synchronisation).  ``workspace`` (a uint8 tensor of at
+    least :func:`workspace_bytes` bytes) is allocated here when not given.
+    ``num_splits`` = 0 lets the library choose the prefix split count.
+    """
+    call = prepare_fwd(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, tree_off,
+                       anc_mask, max_tree=max_tree, max_prefix=max_prefix, scale=scale,
+                       num_splits=num_splits, out=out, lse=lse, workspace=workspace)
+    call.run(stream)
+    return call.out, call.lse

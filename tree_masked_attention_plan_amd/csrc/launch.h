@@ -1,0 +1,51 @@
+// Internal interface between the host dispatch (tree_attn.cpp) and the
+// device code (kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ta {
+
+constexpr int kMaskWords = 4;
+constexpr int kMaxTree = 64 * kMaskWords;
+constexpr int kTreeOk = 0;
+constexpr int kTreeBadOffsets = -1;
+constexpr int kTreeBadPrefix = -2;
+constexpr int kBlockKeys = 64;   // keys per LDS block of the forward kernel
+constexpr int kMaxSplits = 64;   // merge uses one lane per split
+
+struct PlanParams {
+    const int32_t *parent;
+    const int32_t *tree_off;
+    const int32_t *prefix_len;
+    uint64_t *anc_mask;
+    int32_t *depth;
+    int32_t *pos_id;
+    int32_t *status;
+    int32_t B, N, max_tree;
+};
+
+struct FwdParams {
+    const void *q, *k_tree, *v_tree, *k_cache, *v_cache;
+    const int32_t *block_table, *prefix_len, *tree_off;
+    const uint64_t *anc_mask;
+    void *out;
+    float *lse;
+    float *ws_o;     // [nsplit, N, Hq, D] normalised partial outputs
+    float *ws_lse;   // [nsplit, N, Hq] partial log2-sum-exp (scaled scores)
+    int32_t B, N, Hq, Hkv, G, D;
+    int32_t num_pages, max_pages, page_shift, max_tree;
+    int32_t nsplit, chunk;          // prefix split count and keys per split
+    int32_t n_rt;                   // row tiles per (request, kv head)
+    int32_t units, units_per_xcd;   // work units and their per-XCD share
+    float c2;                       // softmax scale * log2(e)
+};
+
+hipError_t launch_plan(const PlanParams &p, hipStream_t stream);
+// nw: waves per workgroup of the bf16 kernel (32 query rows each)
+hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nw, hipStream_t stream);
+// split-K merge of the partials written by launch_fwd (no-op for one split)
+hipError_t launch_merge(const FwdParams &p, hipStream_t stream);
+
+}  // namespace ta

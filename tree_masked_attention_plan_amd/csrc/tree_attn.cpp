@@ -1,0 +1,322 @@
+// Host side of the C ABI declared in include/tree_attn.h: argument checks,
+// the split-K choice, workspace layout and kernel dispatch.  Every check runs
+// before any HIP call so that bad arguments never reach the device.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "tree_attn.h"
+
+namespace {
+
+// Enough workgroups to give each of MI355X's 256 CUs two of them.
+constexpr int64_t kTargetWorkgroups = 512;
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int32_t ilog2(int32_t x)
+{
+    int32_t r = 0;
+    while ((1 << r) < x)
+        ++r;
+    return r;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// waves per workgroup of the bf16 kernel: enough 32-row tiles for the rows
+// of one (request, kv head), at most 4
+int32_t waves_for(int32_t rows)
+{
+    if (rows <= 32)
+        return 1;
+    if (rows <= 64)
+        return 2;
+    return 4;
+}
+
+struct Geometry {
+    int32_t nw, n_rt, nsplit, chunk;
+};
+
+bool sizes_ok(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tree, int32_t max_prefix,
+              ta_dtype_t dtype)
+{
+    return B >= 0 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && (D == 64 || D == 128) &&
+           max_tree >= 0 && max_tree <= TREE_ATTN_MAX_TREE && max_prefix >= 0 &&
+           (dtype == TA_DTYPE_BF16 || dtype == TA_DTYPE_FP32);
+}
+
+// Work decomposition: row tiles per (request, kv head) and prefix splits.
+// Splits are added only while the grid is short of kTargetWorkgroups, keep at
+// least one 64-key block each, and are re-counted after rounding the chunk to
+// whole blocks so that no trailing split is empty.
+Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_tree, int32_t max_prefix,
+                  ta_dtype_t dtype, int32_t forced_splits)
+{
+    Geometry g;
+    const int32_t G = Hq / Hkv;
+    const int32_t rows = max_tree * G;
+    g.nw = waves_for(rows);
+    g.n_rt = rows > 0 ? (int32_t)ceil_div(rows, 32 * g.nw) : 1;
+    int64_t nsplit = 1;
+    if (dtype == TA_DTYPE_BF16 && max_prefix > 0) {
+        if (forced_splits > 0) {
+            nsplit = forced_splits;
+        } else {
+            const int64_t base = (int64_t)B * Hkv * g.n_rt;
+            if (base > 0 && base < kTargetWorkgroups)
+                nsplit = ceil_div(kTargetWorkgroups, base);
+        }
+        const int64_t max_blocks = ceil_div(max_prefix, ta::kBlockKeys);
+        if (nsplit > max_blocks)
+            nsplit = max_blocks;
+        if (nsplit > ta::kMaxSplits)
+            nsplit = ta::kMaxSplits;
+        if (nsplit < 1)
+            nsplit = 1;
+    }
+    int64_t chunk = ceil_div(max_prefix > 0 ? max_prefix : 1, nsplit);
+    chunk = ceil_div(chunk, ta::kBlockKeys) * ta::kBlockKeys;
+    nsplit = max_prefix > 0 ? ceil_div(max_prefix, chunk) : 1;
+    g.nsplit = (int32_t)nsplit;
+    g.chunk = (int32_t)chunk;
+    return g;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t ws_o_bytes(int32_t nsplit, int32_t N, int32_t Hq, int32_t D)
+{
+    return align256((size_t)nsplit * N * Hq * D * sizeof(float));
+}
+
+size_t ws_bytes(const Geometry &g, int32_t N, int32_t Hq, int32_t D)
+{
+    if (g.nsplit <= 1 || N == 0)
+        return 0;
+    return ws_o_bytes(g.nsplit, N, Hq, D) + align256((size_t)g.nsplit * N * Hq * sizeof(float));
+}
+
+ta_status_t check_fwd(const void *q, const void *k_tree, const void *v_tree, const void *k_cache,
+                      const void *v_cache, const int32_t *block_table, const int32_t *prefix_len,
+                      const int32_t *tree_off, const uint64_t *anc_mask, int32_t B, int32_t N,
+                      int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                      int32_t max_pages, int32_t max_tree, int32_t max_prefix, float scale,
+                      ta_dtype_t dtype, int32_t num_splits, const void *out, const float *lse,
+                      const void *workspace, size_t workspace_bytes)
+{
+    if (dtype != TA_DTYPE_BF16 && dtype != TA_DTYPE_FP32)
+        return TA_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128)
+        return TA_ERR_UNSUPPORTED;
+    if (max_tree > TREE_ATTN_MAX_TREE)
+        return TA_ERR_UNSUPPORTED;
+    if (page_size < 1 || page_size > 1024 || !is_pow2(page_size))
+        return TA_ERR_UNSUPPORTED;
+    if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_tree < 0 || max_prefix < 0 ||
+        num_pages < 0 || max_pages < 0 || num_splits < 0 || num_splits > ta::kMaxSplits)
+        return TA_ERR_BAD_SHAPE;
+    if ((int64_t)N > (int64_t)B * max_tree || B > 65535)
+        return TA_ERR_BAD_SHAPE;
+    if ((int64_t)max_prefix > (int64_t)max_pages * page_size)
+        return TA_ERR_BAD_SHAPE;
+    if (max_prefix > 0 && num_pages < 1)
+        return TA_ERR_BAD_SHAPE;
+    // element counts must fit the kernels' 64-bit offsets with room to spare,
+    // and per-row index math uses 32-bit node and head ids
+    if ((int64_t)N * Hq > INT32_MAX || (int64_t)B * max_pages > INT32_MAX ||
+        (int64_t)num_pages * page_size * Hkv * D > ((int64_t)1 << 46))
+        return TA_ERR_BAD_SHAPE;
+    if (!(scale == scale) || isinf(scale))
+        return TA_ERR_BAD_SHAPE;
+    if (B == 0 || N == 0)
+        return TA_OK;
+    if (!q || !k_tree || !v_tree || !prefix_len || !tree_off || !anc_mask || !out || !lse)
+        return TA_ERR_NULL_PTR;
+    if (max_prefix > 0 && (!k_cache || !v_cache || !block_table))
+        return TA_ERR_NULL_PTR;
+    const Geometry g = geometry(B, Hq, Hkv, max_tree, max_prefix, dtype, num_splits);
+    const size_t need = ws_bytes(g, N, Hq, D);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+            return TA_ERR_WORKSPACE;
+    }
+    return TA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tree_attn_abi_version(void) { return TREE_ATTN_ABI_VERSION; }
+
+const char *tree_attn_status_str(int status)
+{
+    switch (status) {
+    case TA_OK: return "ok";
+    case TA_ERR_NULL_PTR: return "a required pointer is NULL";
+    case TA_ERR_BAD_SHAPE: return "inconsistent or out-of-range sizes";
+    case TA_ERR_UNSUPPORTED: return "unsupported configuration (dtype, head_dim, page_size or tree size)";
+    case TA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case TA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+ta_status_t tree_attn_plan(const int32_t *parent, const int32_t *tree_off, const int32_t *prefix_len,
+                           int32_t B, int32_t N, int32_t max_tree, uint64_t *anc_mask, int32_t *depth,
+                           int32_t *pos_id, int32_t *status, void *stream)
+{
+    if (max_tree > TREE_ATTN_MAX_TREE)
+        return TA_ERR_UNSUPPORTED;
+    if (B < 0 || N < 0 || max_tree < 0 || (int64_t)N > (int64_t)B * max_tree)
+        return TA_ERR_BAD_SHAPE;
+    if (B == 0)
+        return TA_OK;
+    if (!tree_off || !prefix_len || !status)
+        return TA_ERR_NULL_PTR;
+    if (N > 0 && (!parent || !anc_mask || !depth || !pos_id))
+        return TA_ERR_NULL_PTR;
+    ta::PlanParams p;
+    p.parent = parent;
+    p.tree_off = tree_off;
+    p.prefix_len = prefix_len;
+    p.anc_mask = anc_mask;
+    p.depth = depth;
+    p.pos_id = pos_id;
+    p.status = status;
+    p.B = B;
+    p.N = N;
+    p.max_tree = max_tree;
+    return ta::launch_plan(p, (hipStream_t)stream) == hipSuccess ? TA_OK : TA_ERR_HIP;
+}
+
+int32_t tree_attn_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tree,
+                             int32_t max_prefix, ta_dtype_t dtype)
+{
+    if (!sizes_ok(B, Hq, Hkv, D, max_tree, max_prefix, dtype))
+        return 0;
+    return geometry(B, Hq, Hkv, max_tree, max_prefix, dtype, 0).nsplit;
+}
+
+size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t max_tree, int32_t max_prefix, ta_dtype_t dtype,
+                                 int32_t num_splits)
+{
+    if (!sizes_ok(B, Hq, Hkv, D, max_tree, max_prefix, dtype) || N < 0 || num_splits < 0 ||
+        num_splits > ta::kMaxSplits)
+        return 0;
+    return ws_bytes(geometry(B, Hq, Hkv, max_tree, max_prefix, dtype, num_splits), N, Hq, D);
+}
+
+ta_status_t tree_attn_fwd_check(const void *q, const void *k_tree, const void *v_tree,
+                                const void *k_cache, const void *v_cache, const int32_t *block_table,
+                                const int32_t *prefix_len, const int32_t *tree_off,
+                                const uint64_t *anc_mask, int32_t B, int32_t N, int32_t Hq,
+                                int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                                int32_t max_pages_per_seq, int32_t max_tree, int32_t max_prefix,
+                                float softmax_scale, ta_dtype_t dtype, int32_t num_splits,
+                                const void *out, const float *lse, const void *workspace,
+                                size_t workspace_bytes)
+{
+    return check_fwd(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, tree_off, anc_mask,
+                     B, N, Hq, Hkv, D, page_size, num_pages, max_pages_per_seq, max_tree, max_prefix,
+                     softmax_scale, dtype, num_splits, out, lse, workspace, workspace_bytes);
+}
+
+}  // extern "C"
+
+namespace {
+
+enum Stage { kStagePartial = 1, kStageMerge = 2, kStageBoth = 3 };
+
+ta_status_t run_fwd(const void *q, const void *k_tree, const void *v_tree, const void *k_cache,
+                    const void *v_cache, const int32_t *block_table, const int32_t *prefix_len,
+                    const int32_t *tree_off, const uint64_t *anc_mask, int32_t B, int32_t N,
+                    int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                    int32_t max_pages_per_seq, int32_t max_tree, int32_t max_prefix,
+                    float softmax_scale, ta_dtype_t dtype, int32_t num_splits, void *out, float *lse,
+                    void *workspace, size_t workspace_bytes, void *stream, int stages)
+{
+    const ta_status_t st = check_fwd(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
+                                     tree_off, anc_mask, B, N, Hq, Hkv, D, page_size, num_pages,
+                                     max_pages_per_seq, max_tree, max_prefix, softmax_scale, dtype,
+                                     num_splits, out, lse, workspace, workspace_bytes);
+    if (st != TA_OK || B == 0 || N == 0)
+        return st;
+    const Geometry g = geometry(B, Hq, Hkv, max_tree, max_prefix, dtype, num_splits);
+    const int64_t units = (int64_t)B * Hkv * g.nsplit * g.n_rt;
+    if (units > INT32_MAX - 8)
+        return TA_ERR_BAD_SHAPE;
+    ta::FwdParams p;
+    p.q = q;
+    p.k_tree = k_tree;
+    p.v_tree = v_tree;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_table = block_table;
+    p.prefix_len = prefix_len;
+    p.tree_off = tree_off;
+    p.anc_mask = anc_mask;
+    p.out = out;
+    p.lse = lse;
+    p.ws_o = nullptr;
+    p.ws_lse = nullptr;
+    if (g.nsplit > 1) {
+        p.ws_o = (float *)workspace;
+        p.ws_lse = (float *)((char *)workspace + ws_o_bytes(g.nsplit, N, Hq, D));
+    }
+    p.B = B;
+    p.N = N;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.G = Hq / Hkv;
+    p.D = D;
+    p.num_pages = num_pages;
+    p.max_pages = max_pages_per_seq;
+    p.page_shift = ilog2(page_size);
+    p.max_tree = max_tree;
+    p.nsplit = g.nsplit;
+    p.chunk = g.chunk;
+    p.n_rt = g.n_rt;
+    p.units = (int32_t)units;
+    p.units_per_xcd = (int32_t)ceil_div(units, 8);
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+    p.c2 = scale * 1.44269504088896340736f;
+    hipStream_t s = (hipStream_t)stream;
+    if (stages & kStagePartial) {
+        if (ta::launch_fwd(p, dtype == TA_DTYPE_FP32, g.nw, s) != hipSuccess)
+            return TA_ERR_HIP;
+    }
+    if (stages & kStageMerge) {
+        if (ta::launch_merge(p, s) != hipSuccess)
+            return TA_ERR_HIP;
+    }
+    return TA_OK;
+}
+
+}  // namespace
+
+#define TA_FWD_PARAMS                                                                               \
+    const void *q, const void *k_tree, const void *v_tree, const void *k_cache, const void *v_cache, \
+        const int32_t *block_table, const int32_t *prefix_len, const int32_t *tree_off,              \
+        const uint64_t *anc_mask, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,          \
+        int32_t page_size, int32_t num_pages, int32_t max_pages_per_seq, int32_t max_tree,           \
+        int32_t max_prefix, float softmax_scale, ta_dtype_t dtype, int32_t num_splits, void *out,    \
+        float *lse, void *workspace, size_t workspace_bytes, void *stream
+#define TA_FWD_ARGS                                                                                 \
+    q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, tree_off, anc_mask, B, N, Hq, Hkv, \
+        D, page_size, num_pages, max_pages_per_seq, max_tree, max_prefix, softmax_scale, dtype,      \
+        num_splits, out, lse, workspace, workspace_bytes, stream
+
+extern "C" {
+
+ta_status_t tree_attn_fwd(TA_FWD_PARAMS) { return run_fwd(TA_FWD_ARGS, kStageBoth); }
+
+ta_status_t tree_attn_fwd_partial(TA_FWD_PARAMS) { return run_fwd(TA_FWD_ARGS, kStagePartial); }
+
+ta_status_t tree_attn_merge(TA_FWD_PARAMS) { return run_fwd(TA_FWD_ARGS, kStageMerge); }
+
+}  // extern "C"
