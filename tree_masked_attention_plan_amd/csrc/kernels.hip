@@ -176,29 +176,81 @@ __device__ __forceinline__ int64_t tree_row(const FwdParams &p, int off, int T, 
 // bf16 forward: D = head dim, NW = waves per workgroup (32 query rows each)
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16): S^T = K Q^T with K as the A
-// operand (from LDS) and Q^T as the B operand (registers, loaded once), so a
-// lane's 16 accumulators are 16 keys of ONE query row (row = lane % 32; the
-// other 16 keys of the 32-key tile are in lane + 32).  Row max / sum then
-// need one cross-half exchange per block instead of a 32-lane reduction, and
-// the probabilities already sit where the B operand of O^T = V^T P^T wants
-// them (same lane, keys along registers).  V is staged in LDS transposed
-// (d-major) in the key order those registers imply.
+// operand (LDS) and Q^T as the B operand (registers, loaded once), so a lane's
+// 16 accumulators are 16 keys of ONE query row (row = lane % 32; the other 16
+// keys of the 32-key tile sit in lane + 32).  Row max / sum need one
+// cross-half exchange per block, and the probabilities already sit where the
+// B operand of O^T = V^T P^T wants them (same lane, keys along registers).
+//
+// K and V blocks of 64 keys stream from HBM straight into LDS with
+// global_load_lds_dwordx4 (no register staging), double-buffered, in their
+// natural [key][d] layout.  Rows are XOR-swizzled in 16-byte units so the
+// operand reads are free of bank conflicts: K with ds_read_b128, V^T with two
+// ds_read_b64_tr_b16 (the gfx950 LDS transpose read) aimed at the exact keys
+// the accumulator layout holds.
 // ---------------------------------------------------------------------------
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p)
-{
-    constexpr int NT = NW * 64;
-    constexpr int KS = D + 8;    // K row stride in LDS (bf16): +16 B breaks bank aliasing
-    constexpr int VS = 64 + 8;   // V^T row stride in LDS (bf16): 144 B per d row
-    constexpr int NKC = D / 16;  // 16-wide d chunks (k steps of S^T = K Q^T)
-    constexpr int NDT = D / 32;  // 32-wide d tiles of O^T
-    constexpr int CH = D / 8;    // 16-byte chunks per K/V row
-    constexpr int KP = (64 * CH + NT - 1) / NT;  // K pieces per thread per block
-    constexpr int VPC = 16 * CH;                 // V pieces (4 keys x 16 B) per block
-    constexpr int VP = (VPC + NT - 1) / NT;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+template <int D>
+struct Layout {
+    static constexpr int ROWB = 2 * D;             // bytes per key row
+    static constexpr int CPR = D / 8;              // 16-byte chunks per row
+    static constexpr int BLK = 64 * ROWB;          // bytes per 64-key block
+    static constexpr int RPI = 1024 / ROWB;        // rows per wave DMA instruction
+    static constexpr int NINST = 64 / RPI;         // DMA instructions per block per tensor
+    // physical 16-byte position of logical chunk c of row r (an involution)
+    __device__ static __forceinline__ int swz_k(int r, int c)
+    {
+        return D == 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+    }
+    __device__ static __forceinline__ int swz_v(int r, int c)
+    {
+        return D == 128 ? (c ^ ((r & 3) << 2)) : (c ^ (((r >> 1) & 1) << 2));
+    }
+};
+
+template <int S>
+struct StageTag {
+    static constexpr int value = S;
+};
+
+// One wave-wide global -> LDS copy of 16 bytes per lane: lane l's bytes land
+// at LDS byte address lds + 16 * l.  Issued as inline asm so that the
+// compiler neither reorders LDS accesses around it nor inserts its own
+// conservative waits; the kernel waits for it explicitly (TA_WAIT_VMCNT).
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt left at their max)
+#define TA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+// SP: pages hold >= 16 tokens, so a 64-key block spans at most 4 pages whose
+// ids are fetched with scalar loads; otherwise each lane loads its own.
+template <int D, int NW, bool SP>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdParams p)
+{
+    using LY = Layout<D>;
+    constexpr int NKC = D / 16;                  // k steps of S^T = K Q^T
+    constexpr int NDT = D / 32;                  // 32-wide d tiles of O^T
+    constexpr int NIW = LY::NINST / NW;          // DMA instructions per wave per tensor
+    static_assert(LY::NINST % NW == 0, "waves must divide the DMA instructions of a block");
+
+    // two stages of K and V blocks, as four distinct arrays so the compiler
+    // can tell that a DMA into one stage never aliases reads of the other
+    __shared__ __attribute__((aligned(1024))) char k_st0[LY::BLK];
+    __shared__ __attribute__((aligned(1024))) char v_st0[LY::BLK];
+    __shared__ __attribute__((aligned(1024))) char k_st1[LY::BLK];
+    __shared__ __attribute__((aligned(1024))) char v_st1[LY::BLK];
 
     Unit u;
     if (!decode_unit(p, u))
@@ -220,10 +272,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p)
     const int qh = u.c * p.G + (row_ok ? my_row - node * p.G : 0);
     const int c = u.c;
     const int32_t *bt = p.block_table + (int64_t)u.b * p.max_pages;
-    const uint16_t *kc_base = (const uint16_t *)p.k_cache;
-    const uint16_t *vc_base = (const uint16_t *)p.v_cache;
-    const uint16_t *kt_base = (const uint16_t *)p.k_tree;
-    const uint16_t *vt_base = (const uint16_t *)p.v_tree;
+    const int64_t head_off = (int64_t)c * D;
+    const int64_t row_stride = (int64_t)p.Hkv * D;   // elements between key rows
+    const int pmask = (1 << p.page_shift) - 1;
 
     // Q^T fragments (B operand): lane holds Q[row][kc*16 + hh*8 .. +8]
     bf16x8 qf[NKC];
@@ -258,102 +309,91 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p)
     const int n_blocks = n_pre + __builtin_popcount(tree_need);
 
     // block k -> (is_tree, first key): prefix blocks first, then tree blocks
-    auto block_of = [&](int k, bool &is_tree, int &start) {
+    auto block_start = [&](int k, bool &is_tree) -> int {
         if (k < n_pre) {
             is_tree = false;
-            start = R.kstart + k * 64;
-        } else {
-            int r = k - n_pre;
-            int m = tree_need;
-            for (int i = 0; i < r; ++i)
-                m &= m - 1;
-            is_tree = true;
-            start = (__builtin_ctz(m)) * 64;
+            return R.kstart + k * 64;
         }
+        int m = tree_need;
+        for (int i = k - n_pre; i > 0; --i)
+            m &= m - 1;
+        is_tree = true;
+        return __builtin_ctz(m) * 64;
     };
 
-    u32x4 kreg[KP];
-    u32x4 vreg[VP][4];
+    // This lane's rows in the DMA instructions of a block: instruction
+    // gi = wv * NIW + i covers rows gi * RPI .. +RPI; the lane's 16 bytes go
+    // to position lane % CPR of row gi * RPI + lane / CPR.
+    int dma_row[NIW];
+#pragma unroll
+    for (int i = 0; i < NIW; ++i)
+        dma_row[i] = (wv * NIW + i) * LY::RPI + lane / LY::CPR;
+    const int dma_pos = lane % LY::CPR;
 
-    auto load_block = [&](int k) {
+    // Page ids are fetched so that no vector load sits between two blocks'
+    // DMA batches (the vmcnt waits below count DMA instructions only): a
+    // 64-key block spans at most 4 pages when pages hold >= 16 tokens, and
+    // those ids are wave-uniform, so scalar loads fetch them; smaller pages
+    // use per-lane loads, consumed before the DMA is issued.
+    auto issue_dma = [&](int k, auto stage) {
         bool is_tree;
-        int start;
-        block_of(k, is_tree, start);
-        const uint16_t *kb = is_tree ? kt_base : kc_base;
-        const uint16_t *vb = is_tree ? vt_base : vc_base;
+        const int start = block_start(k, is_tree);
+        char *kst = decltype(stage)::value == 0 ? k_st0 : k_st1;
+        char *vst = decltype(stage)::value == 0 ? v_st0 : v_st1;
+        const uint16_t *kb = (const uint16_t *)(is_tree ? p.k_tree : p.k_cache);
+        const uint16_t *vb = (const uint16_t *)(is_tree ? p.v_tree : p.v_cache);
+        int pages[4] = {0, 0, 0, 0};
+        const int pfirst = __builtin_amdgcn_readfirstlane(start >> p.page_shift);
+        if (SP && !is_tree) {
+            // the block table is read-only for the whole launch: read it
+            // through the constant address space so these become scalar loads
+            const __attribute__((address_space(4))) int32_t *btc =
+                (const __attribute__((address_space(4))) int32_t *)bt;
+            const int last = min(start + 63, R.kend - 1);
+            const int plast = __builtin_amdgcn_readfirstlane(last >> p.page_shift);
 #pragma unroll
-        for (int it = 0; it < KP; ++it) {
-            const int pc = tid + it * NT;
-            const int key = pc / CH;
-            const int ch = pc % CH;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (pc < 64 * CH) {
-                const int64_t r = is_tree ? tree_row(p, R.off, R.T, start + key, c)
-                                          : prefix_row(p, bt, start + key, R.kend, c);
-                if (r >= 0)
-                    v = *(const u32x4 *)(kb + r + ch * 8);
-            }
-            kreg[it] = v;
+            for (int q = 0; q < 4; ++q)
+                pages[q] = (pfirst + q <= plast) ? btc[pfirst + q] : 0;
         }
 #pragma unroll
-        for (int it = 0; it < VP; ++it) {
-            const int pc = tid + it * NT;
-            const int kq = pc & 15;
-            const int dg = pc >> 4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (pc < VPC) {
-                    const int key = kq * 4 + i;
-                    const int64_t r = is_tree ? tree_row(p, R.off, R.T, start + key, c)
-                                              : prefix_row(p, bt, start + key, R.kend, c);
-                    if (r >= 0)
-                        v = *(const u32x4 *)(vb + r + dg * 8);
+        for (int i = 0; i < NIW; ++i) {
+            const int r = dma_row[i];
+            int64_t off;
+            if (is_tree) {
+                int j = start + r;
+                j = j < R.T ? j : start;   // rows past the tree: a valid, masked row
+                off = (int64_t)(R.off + j) * row_stride + head_off;
+            } else {
+                int t = start + r;
+                t = t < R.kend ? t : start; // keys past the split: a valid, masked row
+                int page;
+                if (SP) {
+                    const int q = (t >> p.page_shift) - pfirst;
+                    page = q == 0 ? pages[0] : (q == 1 ? pages[1] : (q == 2 ? pages[2] : pages[3]));
+                } else {
+                    page = bt[t >> p.page_shift];
                 }
-                vreg[it][i] = v;
+                page = page < 0 ? 0 : (page >= p.num_pages ? p.num_pages - 1 : page);
+                off = (((int64_t)page << p.page_shift) + (t & pmask)) * row_stride + head_off;
             }
+            const int gi = wv * NIW + i;
+            const int ck = LY::swz_k(r, dma_pos);
+            const int cv = LY::swz_v(r, dma_pos);
+            dma16(kb + off + ck * 8, __builtin_amdgcn_readfirstlane(lds_addr(kst) + gi * 1024));
+            dma16(vb + off + cv * 8, __builtin_amdgcn_readfirstlane(lds_addr(vst) + gi * 1024));
         }
     };
 
-    auto store_block = [&]() {
-#pragma unroll
-        for (int it = 0; it < KP; ++it) {
-            const int pc = tid + it * NT;
-            if (pc < 64 * CH) {
-                const int key = pc / CH;
-                const int ch = pc % CH;
-                *(u32x4 *)(Ks + key * KS + ch * 8) = kreg[it];
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < VP; ++it) {
-            const int pc = tid + it * NT;
-            if (pc < VPC) {
-                const int kq = pc & 15;
-                const int dg = pc >> 4;
-                // keys 4kq..4kq+3 land on 4 consecutive positions of the
-                // MFMA key order: tile kt, k-chunk a/2, half hq, sub-quad a&1
-                const int kt = kq >> 3, qq = kq & 7, a = qq >> 1, hq = qq & 1;
-                const int pos = kt * 32 + (a >> 1) * 16 + hq * 8 + (a & 1) * 4;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int wsel = e >> 1;
-                    uint32_t x0 = vreg[it][0][wsel], x1 = vreg[it][1][wsel];
-                    uint32_t x2 = vreg[it][2][wsel], x3 = vreg[it][3][wsel];
-                    uint32_t lo, hi;
-                    if (e & 1) {
-                        lo = (x0 >> 16) | (x1 & 0xffff0000u);
-                        hi = (x2 >> 16) | (x3 & 0xffff0000u);
-                    } else {
-                        lo = (x0 & 0xffffu) | (x1 << 16);
-                        hi = (x2 & 0xffffu) | (x3 << 16);
-                    }
-                    u32x2 w2 = {lo, hi};
-                    *(u32x2 *)(Vt + (dg * 8 + e) * VS + pos) = w2;
-                }
-            }
-        }
-    };
+    // per-lane LDS offsets of the operand reads (row parts fold into immediates)
+    // K (A of S^T): row kt*32 + lr, logical chunk kc*2 + hh
+    // V^T (A of O^T) through the transpose read: source lane (e, q) of its
+    // 16-lane group reads 4 d-values [dcol, dcol+4) of key row
+    //   kt*32 + kc*16 + half*8 + hh*4 + e,  dcol = dt*32 + ((lane/16)&1)*16 + 4q
+    const int te = (lane & 15) >> 2;
+    const int tq = lane & 3;
+    const int v_row_l = hh * 4 + te;                         // row part owned by the lane
+    const int v_chunk_l = ((lane >> 4) & 1) * 2 + (tq >> 1);  // chunk within a 32-wide d tile
+    const int v_half = (tq & 1) * 8;                          // byte offset inside the chunk
 
     f32x16 acc_o[NDT];
 #pragma unroll
@@ -363,109 +403,144 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p)
     float l_run = 0.f;         // this half's partial sum of probabilities
     const float c2 = p.c2;
 
-    if (n_blocks > 0)
-        load_block(0);
-    for (int k = 0; k < n_blocks; ++k) {
-        __syncthreads();   // every wave is done reading the previous block
-        store_block();
-        __syncthreads();
-        if (k + 1 < n_blocks)
-            load_block(k + 1);   // global loads in flight during the math below
-
-        bool is_tree;
-        int start;
-        block_of(k, is_tree, start);
-
-        // which 32-key tiles this wave must compute
-        bool active[2];
-        uint32_t bits[2] = {0xffffffffu, 0xffffffffu};
-        if (is_tree) {
-            const int w = start >> 6;
-            uint64_t word = 0;
-#pragma unroll
-            for (int i = 0; i < kMaskWords; ++i)
-                word = (i == w) ? mw[i] : word;
-            bits[0] = (uint32_t)word;
-            bits[1] = (uint32_t)(word >> 32);
-            active[0] = __ballot(bits[0] != 0u) != 0ull;
-            active[1] = __ballot(bits[1] != 0u) != 0ull;
+    // one block: start the next block's DMA into the other stage, wait for
+    // this block's, then the math on this stage
+    auto step = [&](int k, auto stage) {
+        if (k + 1 < n_blocks) {
+            issue_dma(k + 1, StageTag<1 - decltype(stage)::value>());   // overlaps the math below
+            TA_WAIT_VMCNT(2 * NIW);             // this wave's block-k DMA has landed
         } else {
-            active[0] = start < R.kend;
-            active[1] = start + 32 < R.kend;
+            TA_WAIT_VMCNT(0);
         }
+        __builtin_amdgcn_s_barrier();           // ... and every other wave's too
+            bool is_tree;
+            const int start = block_start(k, is_tree);
+            const char *kst = decltype(stage)::value == 0 ? k_st0 : k_st1;
+            const char *vst = decltype(stage)::value == 0 ? v_st0 : v_st1;
 
-        f32x16 s_acc[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            s_acc[kt] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (active[kt]) {
-#pragma unroll
-                for (int kc = 0; kc < NKC; ++kc) {
-                    const bf16x8 a = *(const bf16x8 *)(Ks + (kt * 32 + lr) * KS + kc * 16 + hh * 8);
-                    s_acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s_acc[kt], 0, 0, 0);
+            // which 32-key tiles this wave must compute
+            bool active[2];
+            uint32_t bits[2] = {0xffffffffu, 0xffffffffu};
+            if (is_tree) {
+                const int w = start >> 6;
+                uint64_t word = 0;
+    #pragma unroll
+                for (int i = 0; i < kMaskWords; ++i)
+                    word = (i == w) ? mw[i] : word;
+                bits[0] = (uint32_t)word;
+                bits[1] = (uint32_t)(word >> 32);
+                active[0] = __ballot(bits[0] != 0u) != 0ull;
+                active[1] = __ballot(bits[1] != 0u) != 0ull;
+            } else {
+                active[0] = true;
+                active[1] = start + 32 < R.kend;
+                const int valid = R.kend - start;   // keys of this block inside the split
+                if (valid < 64) {
+                    bits[0] = valid >= 32 ? 0xffffffffu : ((1u << valid) - 1u);
+                    bits[1] = valid <= 32 ? 0u : (valid >= 64 ? 0xffffffffu : ((1u << (valid - 32)) - 1u));
                 }
             }
-        }
+            const bool masked = is_tree || (start + 64 > R.kend);
 
-        // masks: lane value i of tile kt is key kt*32 + (i/4)*8 + hh*4 + i%4
-        const bool partial = !is_tree && (start + 64 > R.kend);
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kk = (i >> 2) * 8 + hh * 4 + (i & 3);
-                bool vis = active[kt];
-                if (is_tree)
-                    vis = vis && ((bits[kt] >> kk) & 1u);
-                else if (partial)
-                    vis = vis && (start + kt * 32 + kk < R.kend);
-                if (!vis)
-                    s_acc[kt][i] = -INFINITY;
+            f32x16 s_acc[2];
+    #pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                s_acc[kt] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                if (active[kt]) {
+                    const int r = kt * 32 + lr;
+                    const char *krow = kst + r * LY::ROWB;
+    #pragma unroll
+                    for (int kc = 0; kc < NKC; ++kc) {
+                        const bf16x8 a = *(const bf16x8 *)(krow + LY::swz_k(r, kc * 2 + hh) * 16);
+                        s_acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s_acc[kt], 0, 0, 0);
+                    }
+                }
             }
-        }
-
-        // online softmax
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                mx = fmaxf(mx, s_acc[kt][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mx2 = mx * c2;
-        const bool upd = mx2 > m_run + kRescaleSlack;
-        if (__ballot(upd) != 0ull) {
-            const float m_new = upd ? mx2 : m_run;
-            const float alpha = upd ? fast_exp2(m_run - m_new) : 1.0f;
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
+            if (masked) {
+                // lane value i of tile kt is key kt*32 + (i/4)*8 + hh*4 + i%4
+    #pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    const uint32_t bk = active[kt] ? (bits[kt] >> (hh * 4)) : 0u;
+    #pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int kk = (i >> 2) * 8 + (i & 3);
+                        s_acc[kt][i] = ((bk >> kk) & 1u) ? s_acc[kt][i] : -INFINITY;
+                    }
+                }
+            } else if (!active[1]) {
+    #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    acc_o[dt][i] *= alpha;
-            m_run = m_new;
-        }
-        const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            if (!active[kt])
-                continue;
-            bf16x8 pb[2];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float pv = fast_exp2(__builtin_fmaf(s_acc[kt][i], c2, -mu));
-                l_run += pv;
-                pb[i >> 3][i & 7] = (__bf16)pv;
+                    s_acc[1][i] = -INFINITY;
             }
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const bf16x8 a = *(const bf16x8 *)(Vt + (dt * 32 + lr) * VS + kt * 32 + kc * 16 + hh * 8);
-                    acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], acc_o[dt], 0, 0, 0);
+
+            // online softmax
+            float mx = -INFINITY;
+    #pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+    #pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    mx = fmaxf(mx, s_acc[kt][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mx2 = mx * c2;
+            const bool upd = mx2 > m_run + kRescaleSlack;
+            if (__ballot(upd) != 0ull) {
+                const float m_new = upd ? mx2 : m_run;
+                const float alpha = upd ? fast_exp2(m_run - m_new) : 1.0f;
+                l_run *= alpha;
+    #pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+    #pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        acc_o[dt][i] *= alpha;
+                m_run = m_new;
+            }
+            const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+    #pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                if (!active[kt])
+                    continue;
+                bf16x8 pb[2];
+    #pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float pv = fast_exp2(__builtin_fmaf(s_acc[kt][i], c2, -mu));
+                    l_run += pv;
+                    pb[i >> 3][i & 7] = (__bf16)pv;
+                }
+    #pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    const int rbase = kt * 32 + kc * 16 + v_row_l;   // half 0; half 1 is +8
+                    const char *v0 = vst + rbase * LY::ROWB + v_half;
+                    const char *v1 = v0 + 8 * LY::ROWB;
+    #pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        // rows rbase and rbase + 8 share the swizzle
+                        const int pos = LY::swz_v(rbase, dt * 4 + v_chunk_l) * 16;
+                        typedef short i16x4 __attribute__((ext_vector_type(4)));
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4 *)(v0 + pos));
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4 *)(v1 + pos));
+                        typedef short i16x8 __attribute__((ext_vector_type(8)));
+                        const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        const bf16x8 a = __builtin_bit_cast(bf16x8, cat);
+                        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], acc_o[dt], 0, 0, 0);
+                    }
                 }
             }
-        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS reads are done
+        __builtin_amdgcn_s_barrier();         // the stage may now be overwritten
+    };
+
+    // Q and mask words are in registers before the first DMA: the compiler,
+    // which does not see the DMA, then has no load of its own outstanding
+    // inside the loop and inserts no waits there.
+    TA_WAIT_VMCNT(0);
+    if (n_blocks > 0)
+        issue_dma(0, StageTag<0>());
+    for (int k = 0; k < n_blocks; k += 2) {
+        step(k, StageTag<0>());
+        if (k + 1 < n_blocks)
+            step(k + 1, StageTag<1>());
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -678,7 +753,10 @@ hipError_t launch_plan(const PlanParams &p, hipStream_t stream)
 template <int D, int NW>
 static void launch_fwd_bf16_t(const FwdParams &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW>), dim3(p.units_per_xcd * 8), dim3(NW * 64), 0, stream, p);
+    if (p.page_shift >= 4)
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, true>), dim3(p.units_per_xcd * 8), dim3(NW * 64), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, false>), dim3(p.units_per_xcd * 8), dim3(NW * 64), 0, stream, p);
 }
 
 hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nw, hipStream_t stream)
@@ -694,11 +772,13 @@ hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nw, hipStream_t st
     if (p.D == 64) {
         if (nw == 1) launch_fwd_bf16_t<64, 1>(p, stream);
         else if (nw == 2) launch_fwd_bf16_t<64, 2>(p, stream);
-        else launch_fwd_bf16_t<64, 4>(p, stream);
+        else if (nw == 4) launch_fwd_bf16_t<64, 4>(p, stream);
+        else launch_fwd_bf16_t<64, 8>(p, stream);
     } else {
         if (nw == 1) launch_fwd_bf16_t<128, 1>(p, stream);
         else if (nw == 2) launch_fwd_bf16_t<128, 2>(p, stream);
-        else launch_fwd_bf16_t<128, 4>(p, stream);
+        else if (nw == 4) launch_fwd_bf16_t<128, 4>(p, stream);
+        else launch_fwd_bf16_t<128, 8>(p, stream);
     }
     return hipGetLastError();
 }

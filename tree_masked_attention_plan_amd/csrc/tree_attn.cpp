@@ -10,8 +10,10 @@
 
 namespace {
 
-// Enough workgroups to give each of MI355X's 256 CUs two of them.
-constexpr int64_t kTargetWorkgroups = 512;
+// MI355X has 256 CUs; the bf16 kernel runs 2 waves per SIMD, i.e. 8 waves
+// (8 / NW workgroups) per CU.  Splits are added until the grid fills that.
+constexpr int64_t kNumCUs = 256;
+constexpr int64_t kWavesPerCU = 8;
 
 bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -26,14 +28,16 @@ int32_t ilog2(int32_t x)
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // waves per workgroup of the bf16 kernel: enough 32-row tiles for the rows
-// of one (request, kv head), at most 4
+// of one (request, kv head), at most 8 (256 rows share each K/V block in LDS)
 int32_t waves_for(int32_t rows)
 {
     if (rows <= 32)
         return 1;
     if (rows <= 64)
         return 2;
-    return 4;
+    if (rows <= 128)
+        return 4;
+    return 8;
 }
 
 struct Geometry {
@@ -49,7 +53,7 @@ bool sizes_ok(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tree, i
 }
 
 // Work decomposition: row tiles per (request, kv head) and prefix splits.
-// Splits are added only while the grid is short of kTargetWorkgroups, keep at
+// Splits are added only while the grid is short of one full wave of the GPU, keep at
 // least one 64-key block each, and are re-counted after rounding the chunk to
 // whole blocks so that no trailing split is empty.
 Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_tree, int32_t max_prefix,
@@ -66,8 +70,9 @@ Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_tree, int32_t 
             nsplit = forced_splits;
         } else {
             const int64_t base = (int64_t)B * Hkv * g.n_rt;
-            if (base > 0 && base < kTargetWorkgroups)
-                nsplit = ceil_div(kTargetWorkgroups, base);
+            const int64_t target = kNumCUs * (kWavesPerCU / g.nw);
+            if (base > 0 && base < target)
+                nsplit = ceil_div(target, base);
         }
         const int64_t max_blocks = ceil_div(max_prefix, ta::kBlockKeys);
         if (nsplit > max_blocks)
