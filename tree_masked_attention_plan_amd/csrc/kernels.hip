@@ -255,6 +255,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     Unit u;
     if (!decode_unit(p, u))
         return;
+    const int32_t *bt = p.block_table + (int64_t)u.b * p.max_pages;
+    // the block table is read-only for the whole launch: read it through the
+    // constant address space so that page ids come in with scalar loads
+    const __attribute__((address_space(4))) int32_t *btc = (const __attribute__((address_space(4))) int32_t *)bt;
+    // Page ids of the split's first block depend on the split alone, so they
+    // are read together with the request geometry (one memory round trip).
+    int pg0[4] = {0, 0, 0, 0};
+    if (SP && p.max_pages > 0) {
+        const int pf = (u.s * p.chunk) >> p.page_shift;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            pg0[q] = btc[min(pf + q, p.max_pages - 1)];
+    }
     const ReqInfo R = request_info(p, u.b, u.s);
     const int rows = R.T * p.G;
     const int row0 = u.rt * (NW * 32);
@@ -271,42 +284,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int node = row_ok ? my_row / p.G : 0;
     const int qh = u.c * p.G + (row_ok ? my_row - node * p.G : 0);
     const int c = u.c;
-    const int32_t *bt = p.block_table + (int64_t)u.b * p.max_pages;
     const int64_t head_off = (int64_t)c * D;
     const int64_t row_stride = (int64_t)p.Hkv * D;   // elements between key rows
     const int pmask = (1 << p.page_shift) - 1;
 
-    // Q^T fragments (B operand): lane holds Q[row][kc*16 + hh*8 .. +8]
-    bf16x8 qf[NKC];
-    {
-        const uint16_t *qrow = (const uint16_t *)p.q + ((int64_t)(R.off + node) * p.Hq + qh) * D;
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row_ok)
-                v = *(const u32x4 *)(qrow + kc * 16 + hh * 8);
-            qf[kc] = __builtin_bit_cast(bf16x8, v);
-        }
-    }
-
-    // tree blocks this workgroup needs (only the split that owns the tree)
-    const bool owns_tree = (u.s == R.s_tree);
-    uint64_t mw[kMaskWords] = {0, 0, 0, 0};
-    int tree_need = 0;
-    if (owns_tree) {
-        if (row_ok) {
-            const uint64_t *mrow = p.anc_mask + (int64_t)(R.off + node) * kMaskWords;
-#pragma unroll
-            for (int w = 0; w < kMaskWords; ++w)
-                mw[w] = (w * 64 < R.T) ? mrow[w] : 0ull;
-        }
-#pragma unroll
-        for (int w = 0; w < kMaskWords; ++w)
-            if (__syncthreads_or(mw[w] != 0ull))
-                tree_need |= 1 << w;
-    }
     const int n_pre = (R.kend - R.kstart + 63) / 64;
-    const int n_blocks = n_pre + __builtin_popcount(tree_need);
+    int tree_need = 0;
 
     // block k -> (is_tree, first key): prefix blocks first, then tree blocks
     auto block_start = [&](int k, bool &is_tree) -> int {
@@ -330,12 +313,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         dma_row[i] = (wv * NIW + i) * LY::RPI + lane / LY::CPR;
     const int dma_pos = lane % LY::CPR;
 
-    // Page ids are fetched so that no vector load sits between two blocks'
-    // DMA batches (the vmcnt waits below count DMA instructions only): a
-    // 64-key block spans at most 4 pages when pages hold >= 16 tokens, and
-    // those ids are wave-uniform, so scalar loads fetch them; smaller pages
-    // use per-lane loads, consumed before the DMA is issued.
-    auto issue_dma = [&](int k, auto stage) {
+    // Page ids of a prefix block (pages hold >= 16 tokens, so a 64-key block
+    // spans at most 4 pages, and the ids are wave-uniform).
+    auto block_pages = [&](int start, int *pages) {
+        const int pfirst = __builtin_amdgcn_readfirstlane(start >> p.page_shift);
+        const int last = min(start + 63, R.kend - 1);
+        const int plast = __builtin_amdgcn_readfirstlane(last >> p.page_shift);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            pages[q] = (pfirst + q <= plast) ? btc[pfirst + q] : 0;
+    };
+
+    // Issue the copies of block k into a stage.  Page ids are fetched so that
+    // no vector load sits between two blocks' DMA batches (the vmcnt waits
+    // below count DMA instructions only): with SP they come from scalar
+    // loads (or from pre, for the split's first block); smaller pages use
+    // per-lane loads, consumed before the DMA is issued.
+    auto issue_dma = [&](int k, auto stage, const int *pre) {
         bool is_tree;
         const int start = block_start(k, is_tree);
         char *kst = decltype(stage)::value == 0 ? k_st0 : k_st1;
@@ -345,15 +339,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         int pages[4] = {0, 0, 0, 0};
         const int pfirst = __builtin_amdgcn_readfirstlane(start >> p.page_shift);
         if (SP && !is_tree) {
-            // the block table is read-only for the whole launch: read it
-            // through the constant address space so these become scalar loads
-            const __attribute__((address_space(4))) int32_t *btc =
-                (const __attribute__((address_space(4))) int32_t *)bt;
-            const int last = min(start + 63, R.kend - 1);
-            const int plast = __builtin_amdgcn_readfirstlane(last >> p.page_shift);
+            if (pre) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                pages[q] = (pfirst + q <= plast) ? btc[pfirst + q] : 0;
+                for (int q = 0; q < 4; ++q)
+                    pages[q] = pre[q];
+            } else {
+                block_pages(start, pages);
+            }
         }
 #pragma unroll
         for (int i = 0; i < NIW; ++i) {
@@ -384,6 +376,45 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
     };
 
+    // The split's first prefix block is copied before Q and the mask words
+    // are loaded, so the three travel together.
+    const bool early = SP && n_pre > 0;
+    if (early) {
+        // pg0 holds the pages from the split's first key on; rows past kend
+        // fall back to the block's first key, so only valid pages are used
+        issue_dma(0, StageTag<0>(), pg0);
+    }
+
+    // Q^T fragments (B operand): lane holds Q[row][kc*16 + hh*8 .. +8]
+    bf16x8 qf[NKC];
+    {
+        const uint16_t *qrow = (const uint16_t *)p.q + ((int64_t)(R.off + node) * p.Hq + qh) * D;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row_ok)
+                v = *(const u32x4 *)(qrow + kc * 16 + hh * 8);
+            qf[kc] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    // tree blocks this workgroup needs (only the split that owns the tree)
+    const bool owns_tree = (u.s == R.s_tree);
+    uint64_t mw[kMaskWords] = {0, 0, 0, 0};
+    if (owns_tree) {
+        if (row_ok) {
+            const uint64_t *mrow = p.anc_mask + (int64_t)(R.off + node) * kMaskWords;
+#pragma unroll
+            for (int w = 0; w < kMaskWords; ++w)
+                mw[w] = (w * 64 < R.T) ? mrow[w] : 0ull;
+        }
+#pragma unroll
+        for (int w = 0; w < kMaskWords; ++w)
+            if (__syncthreads_or(mw[w] != 0ull))
+                tree_need |= 1 << w;
+    }
+    const int n_blocks = n_pre + __builtin_popcount(tree_need);
+
     // per-lane LDS offsets of the operand reads (row parts fold into immediates)
     // K (A of S^T): row kt*32 + lr, logical chunk kc*2 + hh
     // V^T (A of O^T) through the transpose read: source lane (e, q) of its
@@ -407,7 +438,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // this block's, then the math on this stage
     auto step = [&](int k, auto stage) {
         if (k + 1 < n_blocks) {
-            issue_dma(k + 1, StageTag<1 - decltype(stage)::value>());   // overlaps the math below
+            issue_dma(k + 1, StageTag<1 - decltype(stage)::value>(), nullptr);   // overlaps the math below
             TA_WAIT_VMCNT(2 * NIW);             // this wave's block-k DMA has landed
         } else {
             TA_WAIT_VMCNT(0);
@@ -531,12 +562,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         __builtin_amdgcn_s_barrier();         // the stage may now be overwritten
     };
 
-    // Q and mask words are in registers before the first DMA: the compiler,
+    // Q and mask words are in registers before the loop: the compiler,
     // which does not see the DMA, then has no load of its own outstanding
     // inside the loop and inserts no waits there.
     TA_WAIT_VMCNT(0);
-    if (n_blocks > 0)
-        issue_dma(0, StageTag<0>());
+    if (!early && n_blocks > 0)
+        issue_dma(0, StageTag<0>(), nullptr);
     for (int k = 0; k < n_blocks; k += 2) {
         step(k, StageTag<0>());
         if (k + 1 < n_blocks)
@@ -589,11 +620,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 // ---------------------------------------------------------------------------
 // split-K merge: one wave per (node, q head) row
 //   lse = log2 sum_s 2^{lse_s};  O = sum_s 2^{lse_s - lse} O_s
+// A split's partial row is D fp32 values, read as float4 by D/4 lanes, so one
+// wave-wide load covers SPI = 256/D splits.  All of a batch's loads are issued
+// before any is used: the merge costs one memory latency per 8 * SPI splits,
+// not one per split.
 // ---------------------------------------------------------------------------
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void merge_kernel(FwdParams p)
 {
-    constexpr int PER = D / 64;   // output elements per lane
+    constexpr int LPS = D / 4;        // lanes per split row
+    constexpr int SPI = 64 / LPS;     // splits per wave-wide load
+    constexpr int BATCH = 8;          // loads in flight per lane
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -602,39 +639,63 @@ __global__ __launch_bounds__(256) void merge_kernel(FwdParams p)
     const int qh = row - node * p.Hq;
     if (node >= R.T)
         return;
-    const int nv = R.s_tree + 1;
+    const int nv = R.s_tree + 1;      // splits that hold this request's keys
     const int64_t n = R.off + node;
+    const int64_t split_stride = (int64_t)p.N * p.Hq;   // rows between splits
+    const int64_t r0 = n * p.Hq + qh;
+
     float ls = -INFINITY;
     if (lane < nv)
-        ls = p.ws_lse[((int64_t)lane * p.N + n) * p.Hq + qh];
+        ls = p.ws_lse[lane * split_stride + r0];
     float mx = ls;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
         mx = fmaxf(mx, __shfl_xor(mx, o));
     const float base = (mx == -INFINITY) ? 0.f : mx;
-    float wgt = (lane < nv) ? fast_exp2(ls - base) : 0.f;
+    const float wgt = (lane < nv) ? fast_exp2(ls - base) : 0.f;
     float tot = wgt;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
         tot += __shfl_xor(tot, o);
-    float acc[PER];
+
+    const int grp = lane / LPS;       // which split of a load this lane takes
+    const int dcol = (lane % LPS) * 4;
+    const float *src = p.ws_o + r0 * D + dcol;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nv; s0 += BATCH * SPI) {
+        float4 v[BATCH];
 #pragma unroll
-    for (int e = 0; e < PER; ++e)
-        acc[e] = 0.f;
-    for (int s = 0; s < nv; ++s) {
-        const float ws = __shfl(wgt, s);
-        const float *src = p.ws_o + (((int64_t)s * p.N + n) * p.Hq + qh) * D + lane * PER;
+        for (int i = 0; i < BATCH; ++i) {
+            const int s = s0 + i * SPI + grp;
+            v[i] = s < nv ? *(const float4 *)(src + s * split_stride * D) : float4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-        for (int e = 0; e < PER; ++e)
-            acc[e] += ws * src[e];
+        for (int i = 0; i < BATCH; ++i) {
+            const int s = s0 + i * SPI + grp;
+            const float ws = __shfl(wgt, s < 64 ? s : 0);   // 0 weight past nv
+            acc.x += ws * v[i].x;
+            acc.y += ws * v[i].y;
+            acc.z += ws * v[i].z;
+            acc.w += ws * v[i].w;
+        }
     }
-    const float inv = tot > 0.f ? 1.0f / tot : 0.f;
-    OutT *dst = (OutT *)p.out + (n * p.Hq + qh) * D + lane * PER;
 #pragma unroll
-    for (int e = 0; e < PER; ++e)
-        dst[e] = (OutT)(acc[e] * inv);
+    for (int o = LPS; o < 64; o <<= 1) {
+        acc.x += __shfl_xor(acc.x, o);
+        acc.y += __shfl_xor(acc.y, o);
+        acc.z += __shfl_xor(acc.z, o);
+        acc.w += __shfl_xor(acc.w, o);
+    }
+    if (grp == 0) {
+        const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+        OutT *dst = (OutT *)p.out + r0 * D + dcol;
+        dst[0] = (OutT)(acc.x * inv);
+        dst[1] = (OutT)(acc.y * inv);
+        dst[2] = (OutT)(acc.z * inv);
+        dst[3] = (OutT)(acc.w * inv);
+    }
     if (lane == 0)
-        p.lse[n * p.Hq + qh] = tot > 0.f ? (base + __builtin_log2f(tot)) * kLn2 : -INFINITY;
+        p.lse[r0] = tot > 0.f ? (base + __builtin_log2f(tot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------

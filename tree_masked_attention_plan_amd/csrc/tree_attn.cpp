@@ -27,15 +27,20 @@ int32_t ilog2(int32_t x)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+#ifndef TA_MAX_WAVES
+#define TA_MAX_WAVES 8
+#endif
+
 // waves per workgroup of the bf16 kernel: enough 32-row tiles for the rows
-// of one (request, kv head), at most 8 (256 rows share each K/V block in LDS)
+// of one (request, kv head), at most TA_MAX_WAVES (up to 256 rows share each
+// K/V block in LDS)
 int32_t waves_for(int32_t rows)
 {
     if (rows <= 32)
         return 1;
-    if (rows <= 64)
+    if (rows <= 64 || TA_MAX_WAVES == 2)
         return 2;
-    if (rows <= 128)
+    if (rows <= 128 || TA_MAX_WAVES == 4)
         return 4;
     return 8;
 }
@@ -280,7 +285,8 @@ ta_status_t run_fwd(const void *q, const void *k_tree, const void *v_tree, const
     p.G = Hq / Hkv;
     p.D = D;
     p.num_pages = num_pages;
-    p.max_pages = max_pages_per_seq;
+    // without a prefix the block table may be null: no page is ever read
+    p.max_pages = max_prefix > 0 ? max_pages_per_seq : 0;
     p.page_shift = ilog2(page_size);
     p.max_tree = max_tree;
     p.nsplit = g.nsplit;
