@@ -105,9 +105,13 @@ ta_status_t tree_attn_plan(const int32_t *parent, const int32_t *tree_off,
                            int32_t *pos_id, int32_t *status, void *stream);
 
 /*
- * Number of prefix splits (split-K over the paged prefix, merged by LSE) that
- * tree_attn_fwd uses for these sizes when num_splits = 0 is passed; a pure
- * function of its arguments.  Returns 0 for invalid sizes.
+ * Number of split slots (split-K, merged by LSE) that tree_attn_fwd uses for
+ * these sizes when num_splits = 0 is passed; a pure function of its
+ * arguments.  Returns 0 for invalid sizes.  With one slot a single pass covers
+ * the prefix and the tree.  With S > 1 slots, slots 0 .. S-2 each cover one
+ * chunk of the prefix and slot S-1 covers the tree alone, so the tree phase
+ * runs beside the prefix chunks; a forced count is reduced so that every
+ * prefix chunk holds at least one 64-key block of the longest prefix.
  */
 int32_t tree_attn_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                              int32_t max_tree, int32_t max_prefix, ta_dtype_t dtype);
@@ -150,7 +154,7 @@ size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
  *   prefix_len[b] (<= max_pages_per_seq * page_size).  They size the launch
  *   so no call ever reads device data on the host.
  * softmax_scale <= 0 selects 1/sqrt(D).  num_splits = 0 selects
- *   tree_attn_num_splits(...); 1..64 forces a split count.
+ *   tree_attn_num_splits(...); 1..64 forces a split-slot count (see there).
  * Supported: dtype bf16 or fp32; D in {64, 128}; page_size a power of two in
  *   [1, 1024]; Hq % Hkv == 0.  Anything else is TA_ERR_UNSUPPORTED or
  *   TA_ERR_BAD_SHAPE.

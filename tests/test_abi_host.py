@@ -167,7 +167,7 @@ def test_plan_argument_checks(lib):
 def test_split_choice_for_the_named_workloads():
     # (B, Hq, Hkv, D, max_tree, max_prefix, dtype) -> splits
     assert ta.num_splits(1, 4, 1, 64, 16, 128, __import__("torch").float32) == 1    # tiny (fp32)
-    assert ta.num_splits(1, 32, 8, 128, 16, 2048) == 32                                # chain16
+    assert ta.num_splits(1, 32, 8, 128, 16, 2048) == 17                                # chain16
     assert ta.num_splits(1, 32, 8, 128, 256, 2048) == 8                                # tree256
     assert ta.num_splits(8, 32, 8, 128, 64, 8192) == 4                                 # mixed
     assert ta.num_splits(32, 32, 4, 128, 256, 4096) == 1                               # moe
@@ -179,8 +179,10 @@ def test_split_choice_properties():
             for L in (0, 1, 63, 64, 65, 1000, 8192, 100000):
                 s = ta.num_splits(B, 16, 4, 128, T, L)
                 assert 1 <= s <= 64
-                if L > 0:
-                    assert s <= -(-L // 64)           # each split keeps >= 1 key block
+                if L == 0:
+                    assert s == 1
+                elif s > 1:
+                    assert s - 1 <= -(-L // 64)       # each prefix slot keeps >= 1 key block
                 ws = ta.workspace_bytes(B, B * T, 16, 4, 128, T, L)
                 if s == 1:
                     assert ws == 0

@@ -26,6 +26,7 @@ namespace ta {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -108,6 +109,34 @@ struct Unit {
     int b, c, rt, s;
 };
 
+// The argument copies below are opaque to the compiler, which then no longer
+// knows that their pointers address global memory; accesses through them
+// name the global address space explicitly (global_ rather than flat_
+// instructions, which would also count against lgkmcnt).
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T *gmem(T *ptr)
+{
+    return (__attribute__((address_space(1))) T *)ptr;
+}
+
+// Every kernel argument into scalar registers at once.  Left to itself the
+// compiler loads each field of the argument block where it is first used (or
+// loads it again later instead of keeping it), and each such load is one
+// more dependent scalar-cache round trip.  The empty asm statements make the
+// copies opaque values, so they are loaded together here and kept.
+__device__ __forceinline__ FwdParams load_args(const FwdParams &in)
+{
+    FwdParams a = in;
+    asm volatile("" : "+s"(a.q), "+s"(a.k_tree), "+s"(a.v_tree), "+s"(a.k_cache), "+s"(a.v_cache),
+                      "+s"(a.block_table), "+s"(a.prefix_len), "+s"(a.tree_off), "+s"(a.anc_mask),
+                      "+s"(a.out), "+s"(a.lse), "+s"(a.ws_o), "+s"(a.ws_lse));
+    asm volatile("" : "+s"(a.B), "+s"(a.N), "+s"(a.Hq), "+s"(a.Hkv), "+s"(a.G), "+s"(a.D),
+                      "+s"(a.num_pages), "+s"(a.max_pages), "+s"(a.page_shift), "+s"(a.max_tree),
+                      "+s"(a.nsplit), "+s"(a.chunk), "+s"(a.n_rt), "+s"(a.units),
+                      "+s"(a.units_per_xcd), "+s"(a.c2));
+    return a;
+}
+
 // Workgroups are dealt round-robin to the 8 XCDs (id % 8).  Give each XCD a
 // contiguous run of work units so that the row tiles reading the same K/V
 // chunk run together on one XCD and share its L2.
@@ -127,28 +156,42 @@ __device__ __forceinline__ bool decode_unit(const FwdParams &p, Unit &u)
 }
 
 struct ReqInfo {
-    int off, T, L, s_tree, kstart, kend;
+    int off, T, L, kstart, kend;
+    bool owns_tree;   // this unit runs the request's tree phase
 };
 
 // Request geometry, clamped so that no input can drive an access outside the
-// caller's buffers.
+// caller's buffers.  With one split the unit covers the whole prefix and the
+// tree.  With nsplit > 1 the last split slot holds the tree phase alone and
+// slots 0 .. nsplit-2 cover the prefix in chunks of `chunk` keys (a slot past
+// the request's prefix is empty).
 __device__ __forceinline__ ReqInfo request_info(const FwdParams &p, int b, int s)
 {
+    // read-only for the whole launch: scalar loads through the constant space
+    typedef const __attribute__((address_space(4))) int32_t *cint_p;
     ReqInfo r;
-    int off = p.tree_off[b];
-    int end = p.tree_off[b + 1];
+    int off = ((cint_p)p.tree_off)[b];
+    int end = ((cint_p)p.tree_off)[b + 1];
     off = min(max(off, 0), p.N);
     end = min(max(end, off), p.N);
     r.off = off;
     r.T = min(end - off, p.max_tree);
-    int L = p.prefix_len[b];
+    int L = ((cint_p)p.prefix_len)[b];
     L = min(max(L, 0), p.max_pages << p.page_shift);
     r.L = L;
-    r.s_tree = L > 0 ? min(p.nsplit - 1, (L - 1) / p.chunk) : 0;
-    r.kstart = s * p.chunk;
-    r.kend = (s == r.s_tree) ? L : min(L, r.kstart + p.chunk);
-    if (r.kend < r.kstart)
-        r.kend = r.kstart;
+    if (p.nsplit == 1) {
+        r.kstart = 0;
+        r.kend = L;
+        r.owns_tree = true;
+    } else if (s == p.nsplit - 1) {
+        r.kstart = 0;
+        r.kend = 0;
+        r.owns_tree = true;
+    } else {
+        r.kstart = s * p.chunk;
+        r.kend = max(r.kstart, min(L, r.kstart + p.chunk));
+        r.owns_tree = false;
+    }
     return r;
 }
 
@@ -234,55 +277,96 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 // s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt left at their max)
 #define TA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
+// Workgroup shape: NR row tiles of 32 query rows, each computed by KS waves
+// that split the keys of a step between them (NW = NR * KS waves):
+//   KS = 1: a step is one 64-key block; each wave computes both 32-key tiles
+//   KS = 2: a step is one block; wave slice ks computes tile ks
+//   KS = 4: a step is two blocks; wave slice ks computes tile ks % 2 of the
+//           step's block ks / 2
+// Slices of a row tile keep their own running max / sum / output and combine
+// them through LDS at the end.  Key slices cut the per-wave copy, MFMA and
+// store work for small row counts, where one or two waves would otherwise
+// serialise a block's copy issue and math.
 // SP: pages hold >= 16 tokens, so a 64-key block spans at most 4 pages whose
 // ids are fetched with scalar loads; otherwise each lane loads its own.
-template <int D, int NW, bool SP>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdParams p)
+template <int D, int NR, int KS, bool SP>
+__global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdParams p_arg)
 {
+    const FwdParams p = load_args(p_arg);
     using LY = Layout<D>;
+    constexpr int NW = NR * KS;
+    constexpr int KSB = KS == 4 ? 2 : 1;         // 64-key blocks per step
+    constexpr int NT = KS == 1 ? 2 : 1;          // 32-key tiles per wave per step
     constexpr int NKC = D / 16;                  // k steps of S^T = K Q^T
     constexpr int NDT = D / 32;                  // 32-wide d tiles of O^T
-    constexpr int NIW = LY::NINST / NW;          // DMA instructions per wave per tensor
-    static_assert(LY::NINST % NW == 0, "waves must divide the DMA instructions of a block");
+    constexpr int NI = KSB * LY::NINST;          // DMA instructions per step per tensor
+    constexpr int NIW = NI / NW;                 // ... per wave
+    constexpr int SBYTES = KSB * LY::BLK;        // one stage of K (or of V)
+    static_assert(NI % NW == 0 && NIW >= 1, "waves must divide the DMA instructions of a step");
+    static_assert(NW % KSB == 0, "a wave's DMA instructions must fall in one block");
+    static_assert(NDT % KS == 0, "key slices must divide the output d tiles");
 
-    // two stages of K and V blocks, as four distinct arrays so the compiler
-    // can tell that a DMA into one stage never aliases reads of the other
-    __shared__ __attribute__((aligned(1024))) char k_st0[LY::BLK];
-    __shared__ __attribute__((aligned(1024))) char v_st0[LY::BLK];
-    __shared__ __attribute__((aligned(1024))) char k_st1[LY::BLK];
-    __shared__ __attribute__((aligned(1024))) char v_st1[LY::BLK];
+    // two stages of K and V; after the key loop the same memory holds the
+    // key slices' partial outputs for the combine
+    __shared__ __attribute__((aligned(1024))) char kv_lds[4 * SBYTES];
+    char *const k_st0 = kv_lds;
+    char *const v_st0 = kv_lds + SBYTES;
+    char *const k_st1 = kv_lds + 2 * SBYTES;
+    char *const v_st1 = kv_lds + 3 * SBYTES;
+    // running (max, sum) of every slice's rows, for the final combine
+    __shared__ float2 ml_x[KS > 1 ? NR * KS * 32 : 1];
 
     Unit u;
     if (!decode_unit(p, u))
         return;
     const int32_t *bt = p.block_table + (int64_t)u.b * p.max_pages;
+    typedef const __attribute__((address_space(4))) int32_t *cint_p;
     // the block table is read-only for the whole launch: read it through the
     // constant address space so that page ids come in with scalar loads
-    const __attribute__((address_space(4))) int32_t *btc = (const __attribute__((address_space(4))) int32_t *)bt;
-    // Page ids of the split's first block depend on the split alone, so they
+    const cint_p btc = (cint_p)bt;
+    // Page ids of the split's first step depend on the split alone, so they
     // are read together with the request geometry (one memory round trip).
-    int pg0[4] = {0, 0, 0, 0};
-    if (SP && p.max_pages > 0) {
+    // Without a block table the loads read prefix_len[0] instead (unused).
+    int pg0[4 * KSB];
+    if (SP) {
+        const bool have = p.max_pages > 0;
+        const cint_p src = have ? btc : (cint_p)p.prefix_len;
         const int pf = (u.s * p.chunk) >> p.page_shift;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            pg0[q] = btc[min(pf + q, p.max_pages - 1)];
+        for (int q = 0; q < 4 * KSB; ++q)
+            pg0[q] = src[have ? min(pf + q, p.max_pages - 1) : 0];
     }
     const ReqInfo R = request_info(p, u.b, u.s);
+    if (SP) {
+        // both sets of loads in flight before either is waited for (the
+        // compiler would otherwise sink the page-id loads past the exits)
+#pragma unroll
+        for (int q = 0; q < 4 * KSB; ++q)
+            asm volatile("" : "+s"(pg0[q]));
+    }
     const int rows = R.T * p.G;
-    const int row0 = u.rt * (NW * 32);
-    if (row0 >= rows || u.s > R.s_tree)
+    const int row0 = u.rt * (NR * 32);
+    if (row0 >= rows)
         return;   // uniform across the workgroup
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
+    const int rtw = wv % NR;    // the wave's row tile
+    const int ks = wv / NR;     // the wave's key slice
     const int hh = lane >> 5;   // which half of the wave
     const int lr = lane & 31;   // query row inside the wave's tile
-    const int my_row = row0 + wv * 32 + lr;
+    const int my_row = row0 + rtw * 32 + lr;
     const bool row_ok = my_row < rows;
     const int node = row_ok ? my_row / p.G : 0;
     const int qh = u.c * p.G + (row_ok ? my_row - node * p.G : 0);
+    if (!R.owns_tree && R.kend <= R.kstart) {
+        // an empty prefix split: its rows' partial lse is -inf, so the merge
+        // gives it zero weight without reading the request geometry
+        if (row_ok && hh == 0 && ks == 0)
+            gmem(p.ws_lse)[((int64_t)u.s * p.N + R.off + node) * p.Hq + qh] = -INFINITY;
+        return;   // uniform across the workgroup
+    }
     const int c = u.c;
     const int64_t head_off = (int64_t)c * D;
     const int64_t row_stride = (int64_t)p.Hkv * D;   // elements between key rows
@@ -304,47 +388,52 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         return __builtin_ctz(m) * 64;
     };
 
-    // This lane's rows in the DMA instructions of a block: instruction
-    // gi = wv * NIW + i covers rows gi * RPI .. +RPI; the lane's 16 bytes go
-    // to position lane % CPR of row gi * RPI + lane / CPR.
+    // This wave's DMA instructions of a step: instruction gi = wv * NIW + i
+    // covers rows (gi % NINST) * RPI .. +RPI of the step's block gi / NINST
+    // (the same block for all i); the lane's 16 bytes go to position
+    // lane % CPR of its row.
+    const int dma_blk = (wv * NIW) / LY::NINST;
     int dma_row[NIW];
 #pragma unroll
     for (int i = 0; i < NIW; ++i)
-        dma_row[i] = (wv * NIW + i) * LY::RPI + lane / LY::CPR;
+        dma_row[i] = ((wv * NIW + i) % LY::NINST) * LY::RPI + lane / LY::CPR;
     const int dma_pos = lane % LY::CPR;
 
-    // Page ids of a prefix block (pages hold >= 16 tokens, so a 64-key block
-    // spans at most 4 pages, and the ids are wave-uniform).
-    auto block_pages = [&](int start, int *pages) {
-        const int pfirst = __builtin_amdgcn_readfirstlane(start >> p.page_shift);
-        const int last = min(start + 63, R.kend - 1);
-        const int plast = __builtin_amdgcn_readfirstlane(last >> p.page_shift);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            pages[q] = (pfirst + q <= plast) ? btc[pfirst + q] : 0;
-    };
-
-    // Issue the copies of block k into a stage.  Page ids are fetched so that
-    // no vector load sits between two blocks' DMA batches (the vmcnt waits
-    // below count DMA instructions only): with SP they come from scalar
-    // loads (or from pre, for the split's first block); smaller pages use
+    // Issue this wave's copies of step j into a stage.  Page ids are fetched
+    // so that no vector load sits between two steps' DMA batches (the vmcnt
+    // waits below count DMA instructions only): with SP they come from scalar
+    // loads (or from pre, for the split's first step); smaller pages use
     // per-lane loads, consumed before the DMA is issued.
-    auto issue_dma = [&](int k, auto stage, const int *pre) {
+    auto issue_dma = [&](int j, auto stage, const int *pre) {
+        const int k = j * KSB + dma_blk;
+        if (k >= (n_pre + __builtin_popcount(tree_need)))
+            return;
         bool is_tree;
         const int start = block_start(k, is_tree);
-        char *kst = decltype(stage)::value == 0 ? k_st0 : k_st1;
-        char *vst = decltype(stage)::value == 0 ? v_st0 : v_st1;
+        char *kst = (decltype(stage)::value == 0 ? k_st0 : k_st1) + dma_blk * LY::BLK;
+        char *vst = (decltype(stage)::value == 0 ? v_st0 : v_st1) + dma_blk * LY::BLK;
         const uint16_t *kb = (const uint16_t *)(is_tree ? p.k_tree : p.k_cache);
         const uint16_t *vb = (const uint16_t *)(is_tree ? p.v_tree : p.v_cache);
         int pages[4] = {0, 0, 0, 0};
         const int pfirst = __builtin_amdgcn_readfirstlane(start >> p.page_shift);
         if (SP && !is_tree) {
             if (pre) {
+                // pre[i] is the page of key (split start) + i * page_size
+                const int rel = pfirst - ((u.s * p.chunk) >> p.page_shift);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    int v = 0;
+#pragma unroll
+                    for (int i = 0; i < 4 * KSB; ++i)
+                        v = (i == rel + q) ? pre[i] : v;
+                    pages[q] = v;
+                }
+            } else {
+                const int last = min(start + 63, R.kend - 1);
+                const int plast = __builtin_amdgcn_readfirstlane(last >> p.page_shift);
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    pages[q] = pre[q];
-            } else {
-                block_pages(start, pages);
+                    pages[q] = (pfirst + q <= plast) ? btc[pfirst + q] : 0;
             }
         }
 #pragma unroll
@@ -352,33 +441,35 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             const int r = dma_row[i];
             int64_t off;
             if (is_tree) {
-                int j = start + r;
-                j = j < R.T ? j : start;   // rows past the tree: a valid, masked row
-                off = (int64_t)(R.off + j) * row_stride + head_off;
+                int jn = start + r;
+                jn = jn < R.T ? jn : start;   // rows past the tree: a valid, masked row
+                off = (int64_t)(R.off + jn) * row_stride + head_off;
             } else {
                 int t = start + r;
-                t = t < R.kend ? t : start; // keys past the split: a valid, masked row
+                t = t < R.kend ? t : start;   // keys past the split: a valid, masked row
                 int page;
                 if (SP) {
                     const int q = (t >> p.page_shift) - pfirst;
                     page = q == 0 ? pages[0] : (q == 1 ? pages[1] : (q == 2 ? pages[2] : pages[3]));
                 } else {
-                    page = bt[t >> p.page_shift];
+                    page = gmem(bt)[t >> p.page_shift];
                 }
                 page = page < 0 ? 0 : (page >= p.num_pages ? p.num_pages - 1 : page);
                 off = (((int64_t)page << p.page_shift) + (t & pmask)) * row_stride + head_off;
             }
-            const int gi = wv * NIW + i;
+            const int gl = (wv * NIW + i) % LY::NINST;
             const int ck = LY::swz_k(r, dma_pos);
             const int cv = LY::swz_v(r, dma_pos);
-            dma16(kb + off + ck * 8, __builtin_amdgcn_readfirstlane(lds_addr(kst) + gi * 1024));
-            dma16(vb + off + cv * 8, __builtin_amdgcn_readfirstlane(lds_addr(vst) + gi * 1024));
+            dma16(kb + off + ck * 8, __builtin_amdgcn_readfirstlane(lds_addr(kst) + gl * 1024));
+            dma16(vb + off + cv * 8, __builtin_amdgcn_readfirstlane(lds_addr(vst) + gl * 1024));
         }
     };
 
-    // The split's first prefix block is copied before Q and the mask words
+    // The split's first prefix step is copied before Q and the mask words
     // are loaded, so the three travel together.
-    const bool early = SP && n_pre > 0;
+    // (a unit that owns the tree copies early only a step of prefix blocks:
+    // which tree blocks it needs is known after the mask words arrive)
+    const bool early = SP && n_pre > 0 && (n_pre >= KSB || !R.owns_tree);
     if (early) {
         // pg0 holds the pages from the split's first key on; rows past kend
         // fall back to the block's first key, so only valid pages are used
@@ -388,22 +479,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // Q^T fragments (B operand): lane holds Q[row][kc*16 + hh*8 .. +8]
     bf16x8 qf[NKC];
     {
-        const uint16_t *qrow = (const uint16_t *)p.q + ((int64_t)(R.off + node) * p.Hq + qh) * D;
+        const auto qrow = gmem((const uint16_t *)p.q + ((int64_t)(R.off + node) * p.Hq + qh) * D);
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
             u32x4 v = {0u, 0u, 0u, 0u};
             if (row_ok)
-                v = *(const u32x4 *)(qrow + kc * 16 + hh * 8);
+                v = *(const __attribute__((address_space(1))) u32x4 *)(qrow + kc * 16 + hh * 8);
             qf[kc] = __builtin_bit_cast(bf16x8, v);
         }
     }
 
-    // tree blocks this workgroup needs (only the split that owns the tree)
-    const bool owns_tree = (u.s == R.s_tree);
+    // tree blocks this workgroup needs (only the unit that owns the tree)
     uint64_t mw[kMaskWords] = {0, 0, 0, 0};
-    if (owns_tree) {
+    if (R.owns_tree) {
         if (row_ok) {
-            const uint64_t *mrow = p.anc_mask + (int64_t)(R.off + node) * kMaskWords;
+            const auto mrow = gmem(p.anc_mask + (int64_t)(R.off + node) * kMaskWords);
 #pragma unroll
             for (int w = 0; w < kMaskWords; ++w)
                 mw[w] = (w * 64 < R.T) ? mrow[w] : 0ull;
@@ -414,6 +504,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                 tree_need |= 1 << w;
     }
     const int n_blocks = n_pre + __builtin_popcount(tree_need);
+    const int n_steps = (n_blocks + KSB - 1) / KSB;
 
     // per-lane LDS offsets of the operand reads (row parts fold into immediates)
     // K (A of S^T): row kt*32 + lr, logical chunk kc*2 + hh
@@ -425,6 +516,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int v_row_l = hh * 4 + te;                         // row part owned by the lane
     const int v_chunk_l = ((lane >> 4) & 1) * 2 + (tq >> 1);  // chunk within a 32-wide d tile
     const int v_half = (tq & 1) * 8;                          // byte offset inside the chunk
+    const int my_blk = KS == 4 ? (ks >> 1) : 0;              // the wave's block in a step
 
     f32x16 acc_o[NDT];
 #pragma unroll
@@ -434,83 +526,92 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     float l_run = 0.f;         // this half's partial sum of probabilities
     const float c2 = p.c2;
 
-    // one block: start the next block's DMA into the other stage, wait for
-    // this block's, then the math on this stage
-    auto step = [&](int k, auto stage) {
-        if (k + 1 < n_blocks) {
-            issue_dma(k + 1, StageTag<1 - decltype(stage)::value>(), nullptr);   // overlaps the math below
-            TA_WAIT_VMCNT(2 * NIW);             // this wave's block-k DMA has landed
+    // one step: start the next step's DMA into the other stage, wait for
+    // this step's, then the math on this stage
+    auto step = [&](int j, auto stage) {
+        if (j + 1 < n_steps) {
+            issue_dma(j + 1, StageTag<1 - decltype(stage)::value>(), nullptr);   // overlaps the math below
+            if ((j + 2) * KSB <= n_blocks)
+                TA_WAIT_VMCNT(2 * NIW);         // this wave's step-j DMA has landed
+            else
+                TA_WAIT_VMCNT(0);               // the next step is partial: its count differs
         } else {
             TA_WAIT_VMCNT(0);
         }
         __builtin_amdgcn_s_barrier();           // ... and every other wave's too
+        const int k = j * KSB + my_blk;
+        if (k < n_blocks) {
             bool is_tree;
             const int start = block_start(k, is_tree);
-            const char *kst = decltype(stage)::value == 0 ? k_st0 : k_st1;
-            const char *vst = decltype(stage)::value == 0 ? v_st0 : v_st1;
+            const char *kst = (decltype(stage)::value == 0 ? k_st0 : k_st1) + my_blk * LY::BLK;
+            const char *vst = (decltype(stage)::value == 0 ? v_st0 : v_st1) + my_blk * LY::BLK;
 
-            // which 32-key tiles this wave must compute
-            bool active[2];
-            uint32_t bits[2] = {0xffffffffu, 0xffffffffu};
+            // which 32-key tiles of the block this wave computes
+            int ktile[NT];
+            bool active[NT];
+            uint32_t bits[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                ktile[t] = KS == 1 ? t : (ks & 1);
+                bits[t] = 0xffffffffu;
+            }
             if (is_tree) {
                 const int w = start >> 6;
                 uint64_t word = 0;
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < kMaskWords; ++i)
                     word = (i == w) ? mw[i] : word;
-                bits[0] = (uint32_t)word;
-                bits[1] = (uint32_t)(word >> 32);
-                active[0] = __ballot(bits[0] != 0u) != 0ull;
-                active[1] = __ballot(bits[1] != 0u) != 0ull;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    bits[t] = ktile[t] ? (uint32_t)(word >> 32) : (uint32_t)word;
+                    active[t] = __ballot(bits[t] != 0u) != 0ull;
+                }
             } else {
-                active[0] = true;
-                active[1] = start + 32 < R.kend;
                 const int valid = R.kend - start;   // keys of this block inside the split
-                if (valid < 64) {
-                    bits[0] = valid >= 32 ? 0xffffffffu : ((1u << valid) - 1u);
-                    bits[1] = valid <= 32 ? 0u : (valid >= 64 ? 0xffffffffu : ((1u << (valid - 32)) - 1u));
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int vt = valid - ktile[t] * 32;   // keys of this tile inside the split
+                    active[t] = vt > 0;
+                    if (vt < 32)
+                        bits[t] = vt <= 0 ? 0u : ((1u << vt) - 1u);
                 }
             }
             const bool masked = is_tree || (start + 64 > R.kend);
 
-            f32x16 s_acc[2];
-    #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                s_acc[kt] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                if (active[kt]) {
-                    const int r = kt * 32 + lr;
+            f32x16 s_acc[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                s_acc[t] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                if (active[t]) {
+                    const int r = ktile[t] * 32 + lr;
                     const char *krow = kst + r * LY::ROWB;
-    #pragma unroll
+#pragma unroll
                     for (int kc = 0; kc < NKC; ++kc) {
                         const bf16x8 a = *(const bf16x8 *)(krow + LY::swz_k(r, kc * 2 + hh) * 16);
-                        s_acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s_acc[kt], 0, 0, 0);
+                        s_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s_acc[t], 0, 0, 0);
                     }
                 }
             }
             if (masked) {
-                // lane value i of tile kt is key kt*32 + (i/4)*8 + hh*4 + i%4
-    #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-                    const uint32_t bk = active[kt] ? (bits[kt] >> (hh * 4)) : 0u;
-    #pragma unroll
+                // lane value i of a tile is key tile*32 + (i/4)*8 + hh*4 + i%4
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const uint32_t bk = active[t] ? (bits[t] >> (hh * 4)) : 0u;
+#pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int kk = (i >> 2) * 8 + (i & 3);
-                        s_acc[kt][i] = ((bk >> kk) & 1u) ? s_acc[kt][i] : -INFINITY;
+                        s_acc[t][i] = ((bk >> kk) & 1u) ? s_acc[t][i] : -INFINITY;
                     }
                 }
-            } else if (!active[1]) {
-    #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    s_acc[1][i] = -INFINITY;
             }
 
             // online softmax
             float mx = -INFINITY;
-    #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-    #pragma unroll
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    mx = fmaxf(mx, s_acc[kt][i]);
+                    mx = fmaxf(mx, s_acc[t][i]);
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float mx2 = mx * c2;
             const bool upd = mx2 > m_run + kRescaleSlack;
@@ -518,31 +619,31 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                 const float m_new = upd ? mx2 : m_run;
                 const float alpha = upd ? fast_exp2(m_run - m_new) : 1.0f;
                 l_run *= alpha;
-    #pragma unroll
+#pragma unroll
                 for (int dt = 0; dt < NDT; ++dt)
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 16; ++i)
                         acc_o[dt][i] *= alpha;
                 m_run = m_new;
             }
             const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-    #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                if (!active[kt])
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (!active[t])
                     continue;
                 bf16x8 pb[2];
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float pv = fast_exp2(__builtin_fmaf(s_acc[kt][i], c2, -mu));
+                    const float pv = fast_exp2(__builtin_fmaf(s_acc[t][i], c2, -mu));
                     l_run += pv;
                     pb[i >> 3][i & 7] = (__bf16)pv;
                 }
-    #pragma unroll
+#pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
-                    const int rbase = kt * 32 + kc * 16 + v_row_l;   // half 0; half 1 is +8
+                    const int rbase = ktile[t] * 32 + kc * 16 + v_row_l;   // half 0; half 1 is +8
                     const char *v0 = vst + rbase * LY::ROWB + v_half;
                     const char *v1 = v0 + 8 * LY::ROWB;
-    #pragma unroll
+#pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
                         // rows rbase and rbase + 8 share the swizzle
                         const int pos = LY::swz_v(rbase, dt * 4 + v_chunk_l) * 16;
@@ -558,6 +659,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                     }
                 }
             }
+        }
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS reads are done
         __builtin_amdgcn_s_barrier();         // the stage may now be overwritten
     };
@@ -566,24 +668,99 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // which does not see the DMA, then has no load of its own outstanding
     // inside the loop and inserts no waits there.
     TA_WAIT_VMCNT(0);
-    if (!early && n_blocks > 0)
+    if (!early && n_steps > 0)
         issue_dma(0, StageTag<0>(), nullptr);
-    for (int k = 0; k < n_blocks; k += 2) {
-        step(k, StageTag<0>());
-        if (k + 1 < n_blocks)
-            step(k + 1, StageTag<1>());
+    for (int j = 0; j < n_steps; j += 2) {
+        step(j, StageTag<0>());
+        if (j + 1 < n_steps)
+            step(j + 1, StageTag<1>());
     }
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    float l_tot = l_run + __shfl_xor(l_run, 32);
+    float m_fin = m_run;
+    // d tiles this wave writes: all with one slice, else those with dt % KS == ks
+    auto owns_dt = [&](int dt) { return KS == 1 || (dt % KS) == ks; };
+    if (KS > 1) {
+        // Combine the key slices of each row tile.  Every wave publishes its
+        // rows' (max, sum) and the output tiles it does not own; the stages
+        // are free after the loop's last barrier.
+        float *xo = (float *)kv_lds;   // [NR][KS][NDT - NDT/KS][32 x 32] fp32, lane-major
+        constexpr int NX = NDT - NDT / KS;
+        static_assert(NR * KS * NX * 4096 <= 4 * SBYTES, "combine buffer exceeds the stages");
+        if (hh == 0)
+            ml_x[(rtw * KS + ks) * 32 + lr] = float2{m_run, l_tot};
+        int x = 0;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            if (owns_dt(dt))
+                continue;
+            float4 *dst = (float4 *)(xo + (((rtw * KS + ks) * NX + x) * 1024));
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+                dst[i4 * 64 + lane] = float4{acc_o[dt][i4 * 4 + 0], acc_o[dt][i4 * 4 + 1],
+                                             acc_o[dt][i4 * 4 + 2], acc_o[dt][i4 * 4 + 3]};
+            ++x;
+        }
+        __syncthreads();
+        float mk[KS], lk[KS];
+        float mall = -INFINITY;
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+            const float2 v = ml_x[(rtw * KS + s2) * 32 + lr];
+            mk[s2] = v.x;
+            lk[s2] = v.y;
+            mall = fmaxf(mall, v.x);
+        }
+        const float base = mall == -INFINITY ? 0.f : mall;
+        float ak[KS];
+        float lsum = 0.f, a_own = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+            ak[s2] = mk[s2] == -INFINITY ? 0.f : fast_exp2(mk[s2] - base);
+            lsum += ak[s2] * lk[s2];
+            a_own = s2 == ks ? ak[s2] : a_own;
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            if (!owns_dt(dt))
+                continue;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                acc_o[dt][i] *= a_own;
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) {
+                if (s2 == ks)
+                    continue;
+                // slot of dt among the tiles slice s2 does not own
+                int x2 = 0;
+                for (int d2 = 0; d2 < dt; ++d2)
+                    x2 += (d2 % KS) != s2;
+                const float4 *srcx = (const float4 *)(xo + (((rtw * KS + s2) * NX + x2) * 1024));
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const float4 v = srcx[i4 * 64 + lane];
+                    acc_o[dt][i4 * 4 + 0] += ak[s2] * v.x;
+                    acc_o[dt][i4 * 4 + 1] += ak[s2] * v.y;
+                    acc_o[dt][i4 * 4 + 2] += ak[s2] * v.z;
+                    acc_o[dt][i4 * 4 + 3] += ak[s2] * v.w;
+                }
+            }
+        }
+        l_tot = lsum;
+        m_fin = base;
+    }
     if (!row_ok)
         return;
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    const float lse2 = l_tot > 0.f ? m_run + __builtin_log2f(l_tot) : -INFINITY;
+    const float lse2 = l_tot > 0.f ? m_fin + __builtin_log2f(l_tot) : -INFINITY;
     const int64_t n = R.off + node;
+    const bool lse_writer = hh == 0 && ks == 0;
     if (p.nsplit == 1) {
-        uint16_t *orow = (uint16_t *)p.out + (n * p.Hq + qh) * D;
+        const auto orow = gmem((uint16_t *)p.out + (n * p.Hq + qh) * D);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
+            if (!owns_dt(dt))
+                continue;
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 const __bf16 e0 = (__bf16)(acc_o[dt][i4 * 4 + 0] * inv);
@@ -593,91 +770,97 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                 u32x2 w2;
                 w2[0] = (uint32_t)__builtin_bit_cast(uint16_t, e0) | ((uint32_t)__builtin_bit_cast(uint16_t, e1) << 16);
                 w2[1] = (uint32_t)__builtin_bit_cast(uint16_t, e2) | ((uint32_t)__builtin_bit_cast(uint16_t, e3) << 16);
-                *(u32x2 *)(orow + dt * 32 + i4 * 8 + hh * 4) = w2;
+                *(__attribute__((address_space(1))) u32x2 *)(orow + dt * 32 + i4 * 8 + hh * 4) = w2;
             }
         }
-        if (hh == 0)
-            p.lse[n * p.Hq + qh] = lse2 * kLn2;
+        if (lse_writer)
+            gmem(p.lse)[n * p.Hq + qh] = lse2 * kLn2;
     } else {
-        float *orow = p.ws_o + (((int64_t)u.s * p.N + n) * p.Hq + qh) * D;
+        const auto orow = gmem(p.ws_o + (((int64_t)u.s * p.N + n) * p.Hq + qh) * D);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
+            if (!owns_dt(dt))
+                continue;
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                float4 v;
-                v.x = acc_o[dt][i4 * 4 + 0] * inv;
-                v.y = acc_o[dt][i4 * 4 + 1] * inv;
-                v.z = acc_o[dt][i4 * 4 + 2] * inv;
-                v.w = acc_o[dt][i4 * 4 + 3] * inv;
-                *(float4 *)(orow + dt * 32 + i4 * 8 + hh * 4) = v;
+                const f32x4 v = {acc_o[dt][i4 * 4 + 0] * inv, acc_o[dt][i4 * 4 + 1] * inv,
+                                 acc_o[dt][i4 * 4 + 2] * inv, acc_o[dt][i4 * 4 + 3] * inv};
+                *(__attribute__((address_space(1))) f32x4 *)(orow + dt * 32 + i4 * 8 + hh * 4) = v;
             }
         }
-        if (hh == 0)
-            p.ws_lse[((int64_t)u.s * p.N + n) * p.Hq + qh] = lse2;
+        if (lse_writer)
+            gmem(p.ws_lse)[((int64_t)u.s * p.N + n) * p.Hq + qh] = lse2;
     }
 }
 
 // ---------------------------------------------------------------------------
-// split-K merge: one wave per (node, q head) row
+// split-K merge: one wave per (node, q head) row, over all N * Hq rows
 //   lse = log2 sum_s 2^{lse_s};  O = sum_s 2^{lse_s - lse} O_s
-// A split's partial row is D fp32 values, read as float4 by D/4 lanes, so one
-// wave-wide load covers SPI = 256/D splits.  All of a batch's loads are issued
-// before any is used: the merge costs one memory latency per 8 * SPI splits,
-// not one per split.
+// Every split slot holds an lse for every row (-inf for an empty prefix
+// split), so the merge needs no request geometry.  A split's partial row is D
+// fp32 values, read as float4 by D/4 lanes, so one wave-wide load covers
+// SPI = 256/D splits; the lse and all partial loads of a batch are issued
+// before any is used (one memory latency per 16 * SPI splits).  Partial rows
+// of zero-weight splits may hold stale data and are excluded by a select.
 // ---------------------------------------------------------------------------
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void merge_kernel(FwdParams p)
 {
     constexpr int LPS = D / 4;        // lanes per split row
     constexpr int SPI = 64 / LPS;     // splits per wave-wide load
-    constexpr int BATCH = 8;          // loads in flight per lane
-    const int b = blockIdx.y;
+    constexpr int BATCH = 16;         // loads in flight per lane
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const ReqInfo R = request_info(p, b, 0);
-    const int node = row / p.Hq;
-    const int qh = row - node * p.Hq;
-    if (node >= R.T)
+    const int64_t r0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // n * Hq + qh
+    if (r0 >= (int64_t)p.N * p.Hq)
         return;
-    const int nv = R.s_tree + 1;      // splits that hold this request's keys
-    const int64_t n = R.off + node;
+    const int ns = p.nsplit;
     const int64_t split_stride = (int64_t)p.N * p.Hq;   // rows between splits
-    const int64_t r0 = n * p.Hq + qh;
+    const int grp = lane / LPS;       // which split of a load this lane takes
+    const int dcol = (lane % LPS) * 4;
+    const float *src = p.ws_o + r0 * D + dcol;
 
     float ls = -INFINITY;
-    if (lane < nv)
+    if (lane < ns)
         ls = p.ws_lse[lane * split_stride + r0];
+    float4 v[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+        const int s = i * SPI + grp;
+        v[i] = s < ns ? *(const float4 *)(src + s * split_stride * D) : float4{0.f, 0.f, 0.f, 0.f};
+    }
     float mx = ls;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
         mx = fmaxf(mx, __shfl_xor(mx, o));
     const float base = (mx == -INFINITY) ? 0.f : mx;
-    const float wgt = (lane < nv) ? fast_exp2(ls - base) : 0.f;
+    const float wgt = (lane < ns) ? fast_exp2(ls - base) : 0.f;
     float tot = wgt;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
         tot += __shfl_xor(tot, o);
 
-    const int grp = lane / LPS;       // which split of a load this lane takes
-    const int dcol = (lane % LPS) * 4;
-    const float *src = p.ws_o + r0 * D + dcol;
     float4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nv; s0 += BATCH * SPI) {
-        float4 v[BATCH];
+    auto add = [&](const float4 &x, int s) {
+        const float ws = __shfl(wgt, s & 63);
+        if (s < ns && ws > 0.f) {
+            acc.x += ws * x.x;
+            acc.y += ws * x.y;
+            acc.z += ws * x.z;
+            acc.w += ws * x.w;
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i)
+        add(v[i], i * SPI + grp);
+    for (int s0 = BATCH * SPI; s0 < ns; s0 += BATCH * SPI) {
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
             const int s = s0 + i * SPI + grp;
-            v[i] = s < nv ? *(const float4 *)(src + s * split_stride * D) : float4{0.f, 0.f, 0.f, 0.f};
+            v[i] = s < ns ? *(const float4 *)(src + s * split_stride * D) : float4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            const int s = s0 + i * SPI + grp;
-            const float ws = __shfl(wgt, s < 64 ? s : 0);   // 0 weight past nv
-            acc.x += ws * v[i].x;
-            acc.y += ws * v[i].y;
-            acc.z += ws * v[i].z;
-            acc.w += ws * v[i].w;
-        }
+        for (int i = 0; i < BATCH; ++i)
+            add(v[i], s0 + i * SPI + grp);
     }
 #pragma unroll
     for (int o = LPS; o < 64; o <<= 1) {
@@ -811,16 +994,17 @@ hipError_t launch_plan(const PlanParams &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int D, int NW>
+template <int D, int NR, int KS>
 static void launch_fwd_bf16_t(const FwdParams &p, hipStream_t stream)
 {
+    const dim3 grid(p.units_per_xcd * 8), block(NR * KS * 64);
     if (p.page_shift >= 4)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, true>), dim3(p.units_per_xcd * 8), dim3(NW * 64), 0, stream, p);
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NR, KS, true>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, false>), dim3(p.units_per_xcd * 8), dim3(NW * 64), 0, stream, p);
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NR, KS, false>), grid, block, 0, stream, p);
 }
 
-hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nw, hipStream_t stream)
+hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nr, int ks, hipStream_t stream)
 {
     if (dtype_fp32) {
         const dim3 row_grid((p.max_tree * p.Hq + 3) / 4, p.B);
@@ -830,16 +1014,20 @@ hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nw, hipStream_t st
             hipLaunchKernelGGL((fwd_f32_kernel<128>), row_grid, dim3(256), 0, stream, p);
         return hipGetLastError();
     }
+    // (row tiles, key slices) pairs chosen by the host; anything else is a
+    // host bug and fails the launch
     if (p.D == 64) {
-        if (nw == 1) launch_fwd_bf16_t<64, 1>(p, stream);
-        else if (nw == 2) launch_fwd_bf16_t<64, 2>(p, stream);
-        else if (nw == 4) launch_fwd_bf16_t<64, 4>(p, stream);
-        else launch_fwd_bf16_t<64, 8>(p, stream);
+        if (nr == 1 && ks == 2) launch_fwd_bf16_t<64, 1, 2>(p, stream);
+        else if (nr == 2 && ks == 2) launch_fwd_bf16_t<64, 2, 2>(p, stream);
+        else if (nr == 4 && ks == 2) launch_fwd_bf16_t<64, 4, 2>(p, stream);
+        else if (nr == 8 && ks == 1) launch_fwd_bf16_t<64, 8, 1>(p, stream);
+        else return hipErrorInvalidValue;
     } else {
-        if (nw == 1) launch_fwd_bf16_t<128, 1>(p, stream);
-        else if (nw == 2) launch_fwd_bf16_t<128, 2>(p, stream);
-        else if (nw == 4) launch_fwd_bf16_t<128, 4>(p, stream);
-        else launch_fwd_bf16_t<128, 8>(p, stream);
+        if (nr == 1 && ks == 4) launch_fwd_bf16_t<128, 1, 4>(p, stream);
+        else if (nr == 2 && ks == 4) launch_fwd_bf16_t<128, 2, 4>(p, stream);
+        else if (nr == 4 && ks == 2) launch_fwd_bf16_t<128, 4, 2>(p, stream);
+        else if (nr == 8 && ks == 1) launch_fwd_bf16_t<128, 8, 1>(p, stream);
+        else return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
@@ -848,11 +1036,11 @@ hipError_t launch_merge(const FwdParams &p, hipStream_t stream)
 {
     if (p.nsplit == 1)
         return hipSuccess;
-    const dim3 row_grid((p.max_tree * p.Hq + 3) / 4, p.B);
+    const dim3 grid((unsigned)(((int64_t)p.N * p.Hq + 3) / 4));
     if (p.D == 64)
-        hipLaunchKernelGGL((merge_kernel<64, __bf16>), row_grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((merge_kernel<64, __bf16>), grid, dim3(256), 0, stream, p);
     else
-        hipLaunchKernelGGL((merge_kernel<128, __bf16>), row_grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((merge_kernel<128, __bf16>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -46,8 +46,20 @@ int32_t waves_for(int32_t rows)
 }
 
 struct Geometry {
-    int32_t nw, n_rt, nsplit, chunk;
+    int32_t nr, ks, n_rt, nsplit, chunk;
 };
+
+// key slices per row tile (waves of one row tile that split each step's
+// keys): fill the workgroup up to 8 waves; head_dim 64 has two output d
+// tiles, so at most two slices
+int32_t slices_for(int32_t nr, int32_t D)
+{
+    if (nr >= 8)
+        return 1;
+    if (D == 64 || nr == 4)
+        return 2;
+    return 4;
+}
 
 bool sizes_ok(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tree, int32_t max_prefix,
               ta_dtype_t dtype)
@@ -57,41 +69,53 @@ bool sizes_ok(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tree, i
            (dtype == TA_DTYPE_BF16 || dtype == TA_DTYPE_FP32);
 }
 
-// Work decomposition: row tiles per (request, kv head) and prefix splits.
-// Splits are added only while the grid is short of one full wave of the GPU, keep at
-// least one 64-key block each, and are re-counted after rounding the chunk to
-// whole blocks so that no trailing split is empty.
-Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_tree, int32_t max_prefix,
-                  ta_dtype_t dtype, int32_t forced_splits)
+// Work decomposition: row tiles per (request, kv head) and split slots.
+// With more than one slot, the last slot runs the tree phase alone and the
+// others cover the prefix in equal chunks of whole 64-key blocks, so that the
+// tree and the prefix chunks run side by side.  Slots are added only while
+// the grid is short of one full wave of the GPU, and are re-counted after
+// rounding the chunk to whole blocks so that no trailing prefix slot is empty
+// for the longest prefix.
+Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tree,
+                  int32_t max_prefix, ta_dtype_t dtype, int32_t forced_splits)
 {
     Geometry g;
     const int32_t G = Hq / Hkv;
     const int32_t rows = max_tree * G;
-    g.nw = waves_for(rows);
-    g.n_rt = rows > 0 ? (int32_t)ceil_div(rows, 32 * g.nw) : 1;
-    int64_t nsplit = 1;
+    g.nr = waves_for(rows);
+    g.ks = slices_for(g.nr, D);
+    g.n_rt = rows > 0 ? (int32_t)ceil_div(rows, 32 * g.nr) : 1;
+    const int32_t nw = g.nr * g.ks;
+    // a step of the kernel covers this many prefix keys
+    const int64_t step_keys = (int64_t)ta::kBlockKeys * (g.ks == 4 ? 2 : 1);
+    int64_t nslot = 1;
     if (dtype == TA_DTYPE_BF16 && max_prefix > 0) {
         if (forced_splits > 0) {
-            nsplit = forced_splits;
+            nslot = forced_splits;
         } else {
             const int64_t base = (int64_t)B * Hkv * g.n_rt;
-            const int64_t target = kNumCUs * (kWavesPerCU / g.nw);
+            const int64_t target = kNumCUs * (kWavesPerCU / nw);
             if (base > 0 && base < target)
-                nsplit = ceil_div(target, base);
+                nslot = ceil_div(target, base);
         }
-        const int64_t max_blocks = ceil_div(max_prefix, ta::kBlockKeys);
-        if (nsplit > max_blocks)
-            nsplit = max_blocks;
-        if (nsplit > ta::kMaxSplits)
-            nsplit = ta::kMaxSplits;
-        if (nsplit < 1)
-            nsplit = 1;
+        if (nslot > ta::kMaxSplits)
+            nslot = ta::kMaxSplits;
     }
-    int64_t chunk = ceil_div(max_prefix > 0 ? max_prefix : 1, nsplit);
-    chunk = ceil_div(chunk, ta::kBlockKeys) * ta::kBlockKeys;
-    nsplit = max_prefix > 0 ? ceil_div(max_prefix, chunk) : 1;
-    g.nsplit = (int32_t)nsplit;
-    g.chunk = (int32_t)chunk;
+    g.chunk = (int32_t)(ceil_div(max_prefix > 0 ? max_prefix : 1, step_keys) * step_keys);
+    g.nsplit = 1;
+    if (nslot > 1) {
+        int64_t npre = nslot - 1;
+        const int64_t max_blocks = ceil_div(max_prefix, ta::kBlockKeys);
+        if (npre > max_blocks)
+            npre = max_blocks;
+        // whole steps per chunk where the prefix allows it, whole blocks else
+        const int64_t per = ceil_div(max_prefix, npre);
+        const int64_t unit = per >= step_keys ? step_keys : ta::kBlockKeys;
+        int64_t chunk = ceil_div(per, unit) * unit;
+        npre = ceil_div(max_prefix, chunk);
+        g.nsplit = (int32_t)(npre + 1);
+        g.chunk = (int32_t)chunk;
+    }
     return g;
 }
 
@@ -147,7 +171,7 @@ ta_status_t check_fwd(const void *q, const void *k_tree, const void *v_tree, con
         return TA_ERR_NULL_PTR;
     if (max_prefix > 0 && (!k_cache || !v_cache || !block_table))
         return TA_ERR_NULL_PTR;
-    const Geometry g = geometry(B, Hq, Hkv, max_tree, max_prefix, dtype, num_splits);
+    const Geometry g = geometry(B, Hq, Hkv, D, max_tree, max_prefix, dtype, num_splits);
     const size_t need = ws_bytes(g, N, Hq, D);
     if (need > 0) {
         if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
@@ -208,7 +232,7 @@ int32_t tree_attn_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int3
 {
     if (!sizes_ok(B, Hq, Hkv, D, max_tree, max_prefix, dtype))
         return 0;
-    return geometry(B, Hq, Hkv, max_tree, max_prefix, dtype, 0).nsplit;
+    return geometry(B, Hq, Hkv, D, max_tree, max_prefix, dtype, 0).nsplit;
 }
 
 size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
@@ -218,7 +242,7 @@ size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, 
     if (!sizes_ok(B, Hq, Hkv, D, max_tree, max_prefix, dtype) || N < 0 || num_splits < 0 ||
         num_splits > ta::kMaxSplits)
         return 0;
-    return ws_bytes(geometry(B, Hq, Hkv, max_tree, max_prefix, dtype, num_splits), N, Hq, D);
+    return ws_bytes(geometry(B, Hq, Hkv, D, max_tree, max_prefix, dtype, num_splits), N, Hq, D);
 }
 
 ta_status_t tree_attn_fwd_check(const void *q, const void *k_tree, const void *v_tree,
@@ -256,7 +280,7 @@ ta_status_t run_fwd(const void *q, const void *k_tree, const void *v_tree, const
                                      num_splits, out, lse, workspace, workspace_bytes);
     if (st != TA_OK || B == 0 || N == 0)
         return st;
-    const Geometry g = geometry(B, Hq, Hkv, max_tree, max_prefix, dtype, num_splits);
+    const Geometry g = geometry(B, Hq, Hkv, D, max_tree, max_prefix, dtype, num_splits);
     const int64_t units = (int64_t)B * Hkv * g.nsplit * g.n_rt;
     if (units > INT32_MAX - 8)
         return TA_ERR_BAD_SHAPE;
@@ -298,7 +322,7 @@ ta_status_t run_fwd(const void *q, const void *k_tree, const void *v_tree, const
     p.c2 = scale * 1.44269504088896340736f;
     hipStream_t s = (hipStream_t)stream;
     if (stages & kStagePartial) {
-        if (ta::launch_fwd(p, dtype == TA_DTYPE_FP32, g.nw, s) != hipSuccess)
+        if (ta::launch_fwd(p, dtype == TA_DTYPE_FP32, g.nr, g.ks, s) != hipSuccess)
             return TA_ERR_HIP;
     }
     if (stages & kStageMerge) {
