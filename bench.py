@@ -305,6 +305,59 @@ def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: flo
     return res
 
 
+def _counter_mean_kib(dirpath: str, counter: str, kernel_substr: str) -> tuple:
+    """Mean per-dispatch value of a rocprofv3 counter (summed over its
+    instances) for the dispatches whose kernel name contains kernel_substr."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {dirpath}")
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter or kernel_substr not in r["Kernel_Name"]:
+                continue
+            key = (f, r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} samples for '{kernel_substr}' under {dirpath}")
+    vals = sorted(per.values())
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
+                      copy_write_dir: str, copy_mib: int, out_path: str):
+    """HBM bytes per attention-kernel launch from FETCH_SIZE / WRITE_SIZE
+    passes, each scaled by what the same counter reads for a plain copy of
+    known size (the copy of --calibrate-copy-mib)."""
+    kern = "fwd_bf16_kernel"
+    copy_k = "vectorized_elementwise_kernel"
+    f_kib, nf = _counter_mean_kib(fetch_dir, "FETCH_SIZE", kern)
+    w_kib, nw = _counter_mean_kib(write_dir, "WRITE_SIZE", kern)
+    cf_kib, _ = _counter_mean_kib(copy_fetch_dir, "FETCH_SIZE", copy_k)
+    cw_kib, _ = _counter_mean_kib(copy_write_dir, "WRITE_SIZE", copy_k)
+    copy_bytes = copy_mib << 20
+    f_fac = cf_kib * 1024 / copy_bytes
+    w_fac = cw_kib * 1024 / copy_bytes
+    fetch = f_kib * 1024 / f_fac
+    write = w_kib * 1024 / w_fac
+    w = W.make_config(workload)
+    nsplit = ta.num_splits(w.B, w.Hq, w.Hkv, w.D, w.max_tree, w.max_prefix, w.dtype)
+    alg = work(w, nsplit)["kernel_bytes"]
+    res = {"workload": workload, "kernel": kern, "kernel_src_sha256_16": kernel_hash(),
+           "fetch_kib_per_launch_raw": f_kib, "write_kib_per_launch_raw": w_kib,
+           "launches_fetch": nf, "launches_write": nw,
+           "copy_fetch_factor": f_fac, "copy_write_factor": w_fac,
+           "hbm_read_bytes_per_launch": fetch, "hbm_write_bytes_per_launch": write,
+           "hbm_bytes_per_launch": fetch + write, "algorithmic_bytes_per_launch": alg,
+           "traffic_over_algorithmic": (fetch + write) / alg}
+    with open(out_path, "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(res))
+
+
 def calibrate_copy(mib: int, reps: int):
     """A plain device copy of known size, for scaling HBM byte counters."""
     dev = torch.device("cuda:0")
@@ -329,7 +382,17 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain copy kernel of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
+                    "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/fwd_bf16_kernel_<workload>_traffic.json from rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE passes of this workload and of the copy "
+                         "(--calibrate-copy-mib gives the copy size, default 256); no GPU needed")
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        out = os.path.join(PROFILES, f"fwd_bf16_kernel_{args.workload}_traffic.json")
+        summarize_traffic(args.workload, *args.summarize_traffic, args.calibrate_copy_mib or 256, out)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
