@@ -25,6 +25,7 @@
 namespace ta {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -269,6 +270,24 @@ __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds)
                  : "memory", "m0");
 }
 
+// The same copy addressed as a wave-uniform 64-bit base (scalar registers)
+// plus a per-lane 32-bit byte offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, uint32_t lds)
+{
+    // the base is uniform; read it from lane 0 so that it is certain to sit
+    // in scalar registers whatever the register allocator did with it
+    // (readfirstlane returns a signed int: widen through uint32_t so that the
+    // low half is not sign-extended into the high half)
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(bs), "s"(lds)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
@@ -293,6 +312,12 @@ template <int D, int NR, int KS, bool SP>
 __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdParams p_arg)
 {
     const FwdParams p = load_args(p_arg);
+    // K/V bases as standalone values: a select between two fields of p would
+    // otherwise become a load through a selected address, which pins p in
+    // scratch memory
+    const char *kt_p = (const char *)p.k_tree, *vt_p = (const char *)p.v_tree;
+    const char *kc_p = (const char *)p.k_cache, *vc_p = (const char *)p.v_cache;
+    asm volatile("" : "+s"(kt_p), "+s"(vt_p), "+s"(kc_p), "+s"(vc_p));
     using LY = Layout<D>;
     constexpr int NW = NR * KS;
     constexpr int KSB = KS == 4 ? 2 : 1;         // 64-key blocks per step
@@ -351,7 +376,9 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
+    // the wave index is uniform across the wave; saying so lets everything
+    // derived from it (DMA rows, page choices, LDS bases) live in scalar registers
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rtw = wv % NR;    // the wave's row tile
     const int ks = wv / NR;     // the wave's key slice
     const int hh = lane >> 5;   // which half of the wave
@@ -398,13 +425,29 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     for (int i = 0; i < NIW; ++i)
         dma_row[i] = ((wv * NIW + i) % LY::NINST) * LY::RPI + lane / LY::CPR;
     const int dma_pos = lane % LY::CPR;
+    // SP prefix copies: an instruction's RPI rows lie in one page (pages hold
+    // >= 16 tokens, instructions start at multiples of RPI <= 16), so its
+    // source is a uniform page row plus this lane's constant byte offset
+    // (row inside the instruction, kv head, swizzled 16-byte chunk).
+    const int64_t row_bytes = row_stride * 2;   // bytes between consecutive key rows
+    const int lrow = lane / LY::CPR;                      // row inside an instruction
+    const uint32_t lrow_b = (uint32_t)(lrow * row_bytes);
+    uint32_t kofs[NIW], vofs[NIW];
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) {
+        const uint32_t rb = lrow_b + (uint32_t)(head_off * 2);
+        kofs[i] = rb + LY::swz_k(dma_row[i], dma_pos) * 16;
+        vofs[i] = rb + LY::swz_v(dma_row[i], dma_pos) * 16;
+    }
 
     // Issue this wave's copies of step j into a stage.  Page ids are fetched
     // so that no vector load sits between two steps' DMA batches (the vmcnt
     // waits below count DMA instructions only): with SP they come from scalar
-    // loads (or from pre, for the split's first step); smaller pages use
+    // loads (or from pg0, for the split's first step); smaller pages use
     // per-lane loads, consumed before the DMA is issued.
-    auto issue_dma = [&](int j, auto stage, const int *pre) {
+    // FIRST: the split's first step, whose page ids were read into pg0
+    auto issue_dma = [&](int j, auto stage, auto first) {
+        constexpr bool FIRST = decltype(first)::value != 0;
         const int k = j * KSB + dma_blk;
         if (k >= (n_pre + __builtin_popcount(tree_need)))
             return;
@@ -412,20 +455,20 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
         const int start = block_start(k, is_tree);
         char *kst = (decltype(stage)::value == 0 ? k_st0 : k_st1) + dma_blk * LY::BLK;
         char *vst = (decltype(stage)::value == 0 ? v_st0 : v_st1) + dma_blk * LY::BLK;
-        const uint16_t *kb = (const uint16_t *)(is_tree ? p.k_tree : p.k_cache);
-        const uint16_t *vb = (const uint16_t *)(is_tree ? p.v_tree : p.v_cache);
+        const uint16_t *kb = (const uint16_t *)(is_tree ? kt_p : kc_p);
+        const uint16_t *vb = (const uint16_t *)(is_tree ? vt_p : vc_p);
         int pages[4] = {0, 0, 0, 0};
         const int pfirst = __builtin_amdgcn_readfirstlane(start >> p.page_shift);
         if (SP && !is_tree) {
-            if (pre) {
-                // pre[i] is the page of key (split start) + i * page_size
+            if (FIRST) {
+                // pg0[i] is the page of key (split start) + i * page_size
                 const int rel = pfirst - ((u.s * p.chunk) >> p.page_shift);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     int v = 0;
 #pragma unroll
                     for (int i = 0; i < 4 * KSB; ++i)
-                        v = (i == rel + q) ? pre[i] : v;
+                        v = (i == rel + q) ? pg0[i] : v;
                     pages[q] = v;
                 }
             } else {
@@ -435,6 +478,40 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
                 for (int q = 0; q < 4; ++q)
                     pages[q] = (pfirst + q <= plast) ? btc[pfirst + q] : 0;
             }
+        }
+        if (SP && !is_tree) {
+            // Keys at or past kend are masked, but their rows must still hold
+            // finite values (0 * NaN in P V would poison the output), so in
+            // the ragged last block they are read from a valid key instead:
+            // the instruction's first row, or the block's first key when the
+            // whole instruction lies past kend.
+            const bool ragged = start + 64 > R.kend;   // uniform
+#pragma unroll
+            for (int i = 0; i < NIW; ++i) {
+                const int gl = (wv * NIW + i) % LY::NINST;
+                int t0 = start + gl * LY::RPI;           // first key of the instruction's rows
+                uint32_t ko = kofs[i], vo = vofs[i];
+                if (ragged) {
+                    if (t0 >= R.kend) {
+                        t0 = start;
+                        ko -= lrow_b;
+                        vo -= lrow_b;
+                    } else if (t0 + lrow >= R.kend) {
+                        ko -= lrow_b;
+                        vo -= lrow_b;
+                    }
+                }
+                const int q = (t0 >> p.page_shift) - pfirst;
+                int page = q == 0 ? pages[0] : (q == 1 ? pages[1] : (q == 2 ? pages[2] : pages[3]));
+                page = page < 0 ? 0 : (page >= p.num_pages ? p.num_pages - 1 : page);
+                page = __builtin_amdgcn_readfirstlane(page);   // uniform by construction
+                const int64_t rowo = (((int64_t)page << p.page_shift) + (t0 & pmask)) * row_bytes;
+                const uint32_t ldsk = __builtin_amdgcn_readfirstlane(lds_addr(kst) + gl * 1024);
+                const uint32_t ldsv = __builtin_amdgcn_readfirstlane(lds_addr(vst) + gl * 1024);
+                dma16s(kc_p + rowo, ko, ldsk);
+                dma16s(vc_p + rowo, vo, ldsv);
+            }
+            return;
         }
 #pragma unroll
         for (int i = 0; i < NIW; ++i) {
@@ -473,7 +550,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     if (early) {
         // pg0 holds the pages from the split's first key on; rows past kend
         // fall back to the block's first key, so only valid pages are used
-        issue_dma(0, StageTag<0>(), pg0);
+        issue_dma(0, StageTag<0>(), StageTag<1>());
     }
 
     // Q^T fragments (B operand): lane holds Q[row][kc*16 + hh*8 .. +8]
@@ -530,7 +607,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     // this step's, then the math on this stage
     auto step = [&](int j, auto stage) {
         if (j + 1 < n_steps) {
-            issue_dma(j + 1, StageTag<1 - decltype(stage)::value>(), nullptr);   // overlaps the math below
+            issue_dma(j + 1, StageTag<1 - decltype(stage)::value>(), StageTag<0>());   // overlaps the math below
             if ((j + 2) * KSB <= n_blocks)
                 TA_WAIT_VMCNT(2 * NIW);         // this wave's step-j DMA has landed
             else
@@ -578,18 +655,22 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
             }
             const bool masked = is_tree || (start + 64 > R.kend);
 
+            // the first MFMA of a tile takes the zero accumulator as an inline
+            // constant, so no register is cleared per block
+            const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             f32x16 s_acc[NT];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                s_acc[t] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
                 if (active[t]) {
                     const int r = ktile[t] * 32 + lr;
                     const char *krow = kst + r * LY::ROWB;
 #pragma unroll
                     for (int kc = 0; kc < NKC; ++kc) {
                         const bf16x8 a = *(const bf16x8 *)(krow + LY::swz_k(r, kc * 2 + hh) * 16);
-                        s_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s_acc[t], 0, 0, 0);
+                        s_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], kc == 0 ? zero16 : s_acc[t], 0, 0, 0);
                     }
+                } else {
+                    s_acc[t] = zero16;
                 }
             }
             if (masked) {
@@ -633,11 +714,19 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
                     continue;
                 bf16x8 pb[2];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float pv = fast_exp2(__builtin_fmaf(s_acc[t][i], c2, -mu));
-                    l_run += pv;
-                    pb[i >> 3][i & 7] = (__bf16)pv;
+                for (int i = 0; i < 16; ++i)
+                    pb[i >> 3][i & 7] = (__bf16)fast_exp2(__builtin_fmaf(s_acc[t][i], c2, -mu));
+                // The row sum adds the bf16 probabilities the PV product uses
+                // (numerator and denominator share the same weights), two per
+                // v_dot2_f32_bf16 against (1, 1).
+                const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+                float ls[2] = {0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const bf16x2 pr = {pb[j >> 2][(2 * j) & 7], pb[j >> 2][(2 * j + 1) & 7]};
+                    ls[j & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls[j & 1], false);
                 }
+                l_run += ls[0] + ls[1];
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
                     const int rbase = ktile[t] * 32 + kc * 16 + v_row_l;   // half 0; half 1 is +8
@@ -669,7 +758,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     // inside the loop and inserts no waits there.
     TA_WAIT_VMCNT(0);
     if (!early && n_steps > 0)
-        issue_dma(0, StageTag<0>(), nullptr);
+        issue_dma(0, StageTag<0>(), StageTag<0>());
     for (int j = 0; j < n_steps; j += 2) {
         step(j, StageTag<0>());
         if (j + 1 < n_steps)
