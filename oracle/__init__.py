@@ -43,6 +43,9 @@ def _declare(lib):
     lib.oracle_tree_attn.argtypes = [P, P, P, P, P, P, P, P, P,
                                      i32, i32, i32, i32, i32, i32, i32, i32, ctypes.c_double,
                                      P, ctypes.c_int64, P, P, i32]
+    lib.oracle_commit.restype = ctypes.c_int
+    lib.oracle_commit.argtypes = [P, P, P, P, P, P, P, P, P,
+                                  i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P]
     return lib
 
 
@@ -151,3 +154,46 @@ def tree_attn_workload(w, rows=None, threads=None, scale=None):
     return tree_attn(w.q, w.k_tree, w.v_tree, w.k_cache, w.v_cache, w.block_table,
                      w.prefix_len, w.tree_off, w.parent,
                      scale=w.scale if scale is None else scale, rows=rows, threads=threads)
+
+
+def commit(parent, tree_off, prefix_len, accepted, k_tree, v_tree, k_cache, v_cache, block_table,
+           max_tree: int):
+    """Copy of the accepted paths' K/V rows into the paged caches.
+
+    Works on raw bytes, so any element type is fine.  Returns
+    ``(k_cache', v_cache', new_prefix_len [B] int32, status [B] int32)``;
+    the caches come back as uint8 arrays [num_pages, page_size, Hkv,
+    D * element size] holding the committed bytes (the inputs are not
+    modified)."""
+    lib = _load()
+    parent = _np(parent, np.int32)
+    tree_off = _np(tree_off, np.int32)
+    prefix_len = _np(prefix_len, np.int32)
+    accepted = _np(accepted, np.int32)
+    bt = _np(block_table, np.int32)
+
+    def raw(x):
+        """The tensor's bytes as a fresh uint8 array (last axis = D * element size)."""
+        if hasattr(x, "detach"):
+            return x.detach().cpu().contiguous().view(__import__("torch").uint8).numpy().copy()
+        x = np.ascontiguousarray(x)
+        return x.view(np.uint8).reshape(x.shape[:-1] + (-1,)).copy()
+
+    def elem(x):
+        return x.element_size() if hasattr(x, "element_size") else np.asarray(x).itemsize
+
+    e = elem(k_cache)
+    kt, vt, kc, vc = raw(k_tree), raw(v_tree), raw(k_cache), raw(v_cache)
+    shape = tuple(k_cache.shape)
+    num_pages, page_size, Hkv, D = shape
+    B = len(prefix_len)
+    N = len(parent)
+    new_len = np.zeros(B, dtype=np.int32)
+    status = np.zeros(B, dtype=np.int32)
+    rc = lib.oracle_commit(_ptr(parent), _ptr(tree_off), _ptr(prefix_len), _ptr(accepted), _ptr(kt),
+                           _ptr(vt), _ptr(kc), _ptr(vc), _ptr(bt), B, N, Hkv, D, e, page_size,
+                           num_pages, bt.shape[1] if bt.ndim == 2 else 0, int(max_tree),
+                           _ptr(new_len), _ptr(status))
+    if rc != 0:
+        raise ValueError(f"oracle_commit: error {rc}")
+    return kc, vc, new_len, status

@@ -283,3 +283,110 @@ int oracle_tree_attn(const double *q, const double *k_tree, const double *v_tree
     free(th);
     return J.error;
 }
+
+/*
+ * Commit of the accepted path (the step after verification: JetFlow
+ * technical summary, section 4 and section 1 -- the target model keeps the
+ * longest drafted branch it agrees with and throws the other guesses away; the
+ * kept tokens join the context, so their keys and values join the paged
+ * prefix cache).
+ *
+ * For request b with accepted[b] = a (a local node id, or -1 when nothing was
+ * accepted): the path is a's root path, root first, found by following
+ * parent[] up from a.  The node at depth d (1-based) is the token at position
+ * t = L_b + d - 1 of the sequence, so its K and V rows (all Hkv heads) are
+ * copied byte for byte from k_tree / v_tree row tree_off[b] + node into
+ * k_cache / v_cache at page block_table[b][t / page_size], slot
+ * t % page_size.  new_prefix_len[b] = L_b + depth(a).
+ *
+ * status[b] (checked in this order; on any failure nothing of request b is
+ * written and new_prefix_len[b] = prefix_len[b]):
+ *   -1 bad offsets (as the plan), -2 prefix_len[b] < 0,
+ *   -3 accepted[b] outside [-1, T_b),
+ *   k > 0: node k-1 on the path has a parent outside [-1, k-1),
+ *   -4 a block-table entry for one of the positions L_b .. L_b + depth - 1
+ *      lies beyond max_pages or names a page outside [0, num_pages).
+ * Rows are elem_size * Hkv * D bytes.  Returns ORACLE_ERR_ARGS for bad sizes.
+ */
+#define ORACLE_COMMIT_BAD_ACCEPTED (-3)
+#define ORACLE_COMMIT_BAD_PAGE (-4)
+
+int oracle_commit(const int32_t *parent, const int32_t *tree_off, const int32_t *prefix_len,
+                  const int32_t *accepted, const void *k_tree, const void *v_tree, void *k_cache,
+                  void *v_cache, const int32_t *block_table, int32_t B, int32_t N, int32_t Hkv,
+                  int32_t D, int32_t elem_size, int32_t page_size, int32_t num_pages,
+                  int32_t max_pages, int32_t max_tree, int32_t *new_prefix_len, int32_t *status)
+{
+    if (B < 0 || N < 0 || Hkv < 1 || D < 1 || elem_size < 1 || page_size < 1 || num_pages < 0 ||
+        max_pages < 0 || max_tree < 0 || max_tree > ORACLE_MAX_TREE)
+        return ORACLE_ERR_ARGS;
+    const size_t row_bytes = (size_t)elem_size * (size_t)Hkv * (size_t)D;
+    int32_t path[ORACLE_MAX_TREE];
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t off = tree_off[b];
+        const int32_t end = tree_off[b + 1];
+        const int32_t T = end - off;
+        const int32_t L = prefix_len[b];
+        new_prefix_len[b] = L;
+        if (T < 0 || T > max_tree || off < 0 || end > N || (b == 0 && off != 0) ||
+            (b == B - 1 && end != N)) {
+            status[b] = ORACLE_TREE_BAD_OFFSETS;
+            continue;
+        }
+        if (L < 0) {
+            status[b] = ORACLE_TREE_BAD_PREFIX;
+            continue;
+        }
+        const int32_t a = accepted[b];
+        if (a < -1 || a >= T) {
+            status[b] = ORACLE_COMMIT_BAD_ACCEPTED;
+            continue;
+        }
+        /* walk up from a, recording the path leaf first */
+        int32_t depth = 0, bad = 0;
+        for (int32_t i = a; i >= 0;) {
+            const int32_t p = parent[off + i];
+            if (p < -1 || p >= i) {
+                bad = i + 1;
+                break;
+            }
+            path[depth++] = i;
+            i = p;
+        }
+        if (bad) {
+            status[b] = bad;
+            continue;
+        }
+        /* every page the path's positions land in must exist */
+        for (int32_t d = 0; d < depth; ++d) {
+            const int64_t t = (int64_t)L + d;
+            const int64_t slot_page = t / page_size;
+            if (slot_page >= max_pages) {
+                bad = 1;
+                break;
+            }
+            const int32_t page = block_table[(int64_t)b * max_pages + slot_page];
+            if (page < 0 || page >= num_pages) {
+                bad = 1;
+                break;
+            }
+        }
+        if (bad) {
+            status[b] = ORACLE_COMMIT_BAD_PAGE;
+            continue;
+        }
+        /* copy root first: the node at depth d is path[depth - d] */
+        for (int32_t d = 1; d <= depth; ++d) {
+            const int32_t node = path[depth - d];
+            const int64_t t = (int64_t)L + d - 1;
+            const int32_t page = block_table[(int64_t)b * max_pages + t / page_size];
+            const int64_t dst_row = (int64_t)page * page_size + t % page_size;
+            const int64_t src_row = (int64_t)off + node;
+            memcpy((char *)k_cache + dst_row * row_bytes, (const char *)k_tree + src_row * row_bytes, row_bytes);
+            memcpy((char *)v_cache + dst_row * row_bytes, (const char *)v_tree + src_row * row_bytes, row_bytes);
+        }
+        new_prefix_len[b] = L + depth;
+        status[b] = ORACLE_TREE_OK;
+    }
+    return ORACLE_OK;
+}

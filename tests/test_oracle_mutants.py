@@ -7,6 +7,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_commit as commit_pins
 from tests import test_oracle_pins as pins
 
 # (description, exact text in tree_attn_oracle.c, replacement)
@@ -32,6 +33,15 @@ MUTANTS = [
     ("status index not one-based", "status[b] = first_bad + 1;", "status[b] = first_bad;"),
     ("q row of the wrong head", "const double *qrow = J->q + ((int64_t)node * J->Hq + h) * D;",
      "const double *qrow = J->q + ((int64_t)node * J->Hq + (h + 1) % J->Hq) * D;"),
+    ("commit: path written leaf first", "const int32_t node = path[depth - d];", "const int32_t node = path[d - 1];"),
+    ("commit: position off by one", "const int64_t t = (int64_t)L + d - 1;\n            const int32_t page",
+     "const int64_t t = (int64_t)L + d;\n            const int32_t page"),
+    ("commit: accepted node itself left out", "path[depth++] = i;\n            i = p;",
+     "if (i != a) path[depth++] = i;\n            i = p;"),
+    ("commit: V not copied", "memcpy((char *)v_cache + dst_row * row_bytes", "if (0) memcpy((char *)v_cache + dst_row * row_bytes"),
+    ("commit: new length not advanced", "new_prefix_len[b] = L + depth;", "new_prefix_len[b] = L;"),
+    ("commit: page checks skipped", "status[b] = ORACLE_COMMIT_BAD_PAGE;\n            continue;",
+     "(void)0;"),
 ]
 
 PIN_CALLS = [
@@ -45,6 +55,11 @@ PIN_CALLS = [
     pins.test_zero_keys_closed_form,
     pins.test_one_visible_key,
     pins.test_non_ancestors_do_not_leak,
+    commit_pins.test_chain_commits_nodes_in_order,
+    lambda: commit_pins.test_rows_are_the_accepted_nodes_ancestors_by_depth(__import__("torch").bfloat16, 16),
+    commit_pins.test_nothing_accepted_changes_nothing,
+    commit_pins.test_two_commits_equal_one_flat_append,
+    commit_pins.test_error_statuses_write_nothing_for_that_request,
 ]
 
 

@@ -220,7 +220,8 @@ def make_workload(name: str, prefix_lens: Sequence[int], trees: Sequence[np.ndar
                   Hq: int, Hkv: int, D: int, dtype: torch.dtype, seed: int,
                   page_size: int = PAGE_SIZE, spare_frac: float = 0.10,
                   sentinel: float = float("nan"),
-                  perm_rng: Optional[np.random.Generator] = None) -> Workload:
+                  perm_rng: Optional[np.random.Generator] = None,
+                  reserve_tokens: int = 0) -> Workload:
     """Assemble a batch: paged prefix K/V in one shuffled pool, tree K/V, Q.
 
     The pool holds exactly the live pages plus ``spare_frac`` spare pages; the
@@ -228,7 +229,9 @@ def make_workload(name: str, prefix_lens: Sequence[int], trees: Sequence[np.ndar
     request's pages are scattered and interleaved with the others.  Spare
     pages, slots past a request's prefix length in its last page, and unused
     block-table entries (-1) are filled with ``sentinel`` (NaN by default) so
-    that any read of them poisons the output.
+    that any read of them poisons the output.  ``reserve_tokens`` extra
+    token slots per request get live pages too (room for committing accepted
+    tree tokens after the prefix); their slots hold the sentinel.
     """
     B = len(prefix_lens)
     assert len(trees) == B
@@ -239,7 +242,7 @@ def make_workload(name: str, prefix_lens: Sequence[int], trees: Sequence[np.ndar
     N = int(tree_off[-1])
     parent = np.concatenate([np.asarray(t, dtype=np.int32) for t in trees]) if N else np.zeros(0, np.int32)
 
-    pages_per = [(L + page_size - 1) // page_size for L in prefix_lens]
+    pages_per = [(L + reserve_tokens + page_size - 1) // page_size for L in prefix_lens]
     live = int(sum(pages_per))
     num_pages = max(1, live + int(math.ceil(spare_frac * live)))
     prng = perm_rng if perm_rng is not None else rng_for(seed, _STREAM_PERM)
@@ -299,3 +302,14 @@ def make_config(name: str, seed: Optional[int] = None) -> Workload:
         trees = [best_first_tree(256, trng) for _ in range(32)]
         return make_workload(name, [4096] * 32, trees, 32, 4, 128, torch.bfloat16, seed)
     raise ValueError(name)
+
+
+def random_accepted(trees: Sequence[np.ndarray], rng: np.random.Generator,
+                    p_none: float = 0.1) -> np.ndarray:
+    """One accepted node per tree (local id), uniform over its nodes, or -1
+    (nothing accepted) with probability ``p_none`` or for an empty tree."""
+    out = np.full(len(trees), -1, dtype=np.int32)
+    for b, t in enumerate(trees):
+        if len(t) and rng.random() >= p_none:
+            out[b] = int(rng.integers(0, len(t)))
+    return out
