@@ -10,7 +10,9 @@ import oracle
 from tests import test_oracle_commit as commit_pins
 from tests import test_oracle_pins as pins
 
-# (description, exact text in tree_attn_oracle.c, replacement)
+# (description, exact text in tree_attn_oracle.c, replacement).  Mutants run in
+# this process, so none may remove a bounds check (an out-of-bounds write
+# would corrupt the test process itself).
 MUTANTS = [
     ("node does not see itself",
      "for (int32_t j = i; j != -1; j = J->parent[off + j]) {\n        if (j < 0",
@@ -40,8 +42,8 @@ MUTANTS = [
      "if (i != a) path[depth++] = i;\n            i = p;"),
     ("commit: V not copied", "memcpy((char *)v_cache + dst_row * row_bytes", "if (0) memcpy((char *)v_cache + dst_row * row_bytes"),
     ("commit: new length not advanced", "new_prefix_len[b] = L + depth;", "new_prefix_len[b] = L;"),
-    ("commit: page checks skipped", "status[b] = ORACLE_COMMIT_BAD_PAGE;\n            continue;",
-     "(void)0;"),
+    ("commit: missing page reported as a bad accepted node", "status[b] = ORACLE_COMMIT_BAD_PAGE;",
+     "status[b] = ORACLE_COMMIT_BAD_ACCEPTED;"),
 ]
 
 PIN_CALLS = [
