@@ -175,6 +175,51 @@ ta_status_t tree_attn_fwd(const void *q, const void *k_tree, const void *v_tree,
                           size_t workspace_bytes, void *stream);
 
 /*
+ * tree_attn_commit -- append each request's accepted path to its paged cache.
+ *
+ * After verification the target model keeps the longest drafted branch it
+ * agrees with and discards the rest (JetFlow technical summary, sections 1
+ * and 4); the kept tokens join the context, so their keys and values join the
+ * paged prefix.  For request b with accepted[b] = a (a local node id, or -1
+ * when nothing was accepted), every node j on a's root path -- bit j of
+ * anc_mask[tree_off[b] + a] -- is the token at position
+ *   t = prefix_len[b] + depth[tree_off[b] + j] - 1,
+ * and its K and V rows (all Hkv heads) are copied byte for byte from
+ * k_tree / v_tree row tree_off[b] + j into k_cache / v_cache at page
+ * block_table[b, t / page_size], slot t % page_size.  Then
+ * new_prefix_len[b] = prefix_len[b] + depth[tree_off[b] + a].
+ *
+ * anc_mask, depth (device): as written by tree_attn_plan for these trees.
+ * tree_off [B+1], prefix_len [B], accepted [B] i32 (device).
+ * k_tree, v_tree [N, Hkv, D]; k_cache, v_cache [num_pages, page_size, Hkv, D]
+ *   (device, dtype; all 16-byte aligned).  The caches are written in place.
+ * block_table [B, max_pages_per_seq] i32 (device): must hold pages for the
+ *   positions prefix_len[b] .. prefix_len[b] + depth(a) - 1.
+ * new_prefix_len [B], status [B] i32 (device, written):
+ *   status[b] = 0, TA_TREE_BAD_OFFSETS, TA_TREE_BAD_PREFIX,
+ *   TA_COMMIT_BAD_ACCEPTED (a outside [-1, T_b)), TA_COMMIT_BAD_PAGE (a
+ *   needed block-table entry is missing, beyond max_pages_per_seq or outside
+ *   [0, num_pages)), or TA_COMMIT_BAD_PLAN (anc_mask / depth do not name one
+ *   node per depth on a's path: they are not a plan of these trees).  On any
+ *   non-zero status nothing of request b is written and new_prefix_len[b] =
+ *   prefix_len[b].
+ * Supported: dtype bf16 or fp32, Hkv * D * element size a multiple of 16
+ *   bytes, page_size a power of two in [1, 1024], max_tree <= 256.
+ * Requests must write disjoint cache slots (distinct pages); overlapping
+ * writes land in an unspecified order.
+ */
+#define TA_COMMIT_BAD_ACCEPTED (-3)
+#define TA_COMMIT_BAD_PAGE (-4)
+#define TA_COMMIT_BAD_PLAN (-5)
+ta_status_t tree_attn_commit(const uint64_t *anc_mask, const int32_t *depth, const int32_t *tree_off,
+                             const int32_t *prefix_len, const int32_t *accepted, const void *k_tree,
+                             const void *v_tree, void *k_cache, void *v_cache,
+                             const int32_t *block_table, int32_t B, int32_t N, int32_t Hkv, int32_t D,
+                             int32_t page_size, int32_t num_pages, int32_t max_pages_per_seq,
+                             int32_t max_tree, ta_dtype_t dtype, int32_t *new_prefix_len,
+                             int32_t *status, void *stream);
+
+/*
  * The two stages of tree_attn_fwd, for callers that schedule or time them
  * separately.  Both take exactly the arguments of tree_attn_fwd and run the
  * same host checks; tree_attn_fwd is tree_attn_fwd_partial followed by

@@ -192,3 +192,41 @@ def test_split_choice_properties():
     assert ta.workspace_bytes(1, 16, 32, 8, 128, 16, 2048, num_splits=3) > 0
     assert ta.workspace_bytes(1, 16, 32, 8, 128, 16, 0) == 0
     assert ta.workspace_bytes(1, 16, 32, 8, 128, 16, 2048, num_splits=1) == 0
+
+
+def commit_call(lib, **over):
+    a = dict(anc=FAKE, depth=FAKE, tree_off=FAKE, prefix_len=FAKE, accepted=FAKE, k_tree=FAKE,
+             v_tree=FAKE, k_cache=FAKE, v_cache=FAKE, block_table=FAKE, B=2, N=10, Hkv=8, D=128,
+             page_size=16, num_pages=100, max_pages=8, max_tree=8, dtype=BF16, new_len=FAKE,
+             status=FAKE)
+    a.update(over)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.tree_attn_commit(P(a["anc"]), P(a["depth"]), P(a["tree_off"]), P(a["prefix_len"]),
+                                P(a["accepted"]), P(a["k_tree"]), P(a["v_tree"]), P(a["k_cache"]),
+                                P(a["v_cache"]), P(a["block_table"]), a["B"], a["N"], a["Hkv"], a["D"],
+                                a["page_size"], a["num_pages"], a["max_pages"], a["max_tree"], a["dtype"],
+                                P(a["new_len"]), P(a["status"]), None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=7), TA_ERR_UNSUPPORTED),
+    (dict(max_tree=257, N=10), TA_ERR_UNSUPPORTED),
+    (dict(page_size=24), TA_ERR_UNSUPPORTED),
+    (dict(Hkv=1, D=4), TA_ERR_UNSUPPORTED),        # 8-byte rows cannot move 16 bytes at a time
+    (dict(N=17), TA_ERR_BAD_SHAPE),                # N > B * max_tree
+    (dict(B=-1), TA_ERR_BAD_SHAPE),
+    (dict(Hkv=0), TA_ERR_BAD_SHAPE),
+    (dict(accepted=None), TA_ERR_NULL_PTR),
+    (dict(block_table=None), TA_ERR_NULL_PTR),
+    (dict(status=None), TA_ERR_NULL_PTR),
+    (dict(anc=None), TA_ERR_NULL_PTR),
+    (dict(k_cache=FAKE + 8), TA_ERR_BAD_SHAPE),     # rows are copied 16 bytes at a time
+])
+def test_commit_rejects_before_launch(lib, over, code):
+    assert commit_call(lib, **over) == code
+
+
+def test_commit_empty_batch_is_noop(lib):
+    assert commit_call(lib, B=0, N=0, anc=None, depth=None, tree_off=None, prefix_len=None,
+                       accepted=None, k_tree=None, v_tree=None, k_cache=None, v_cache=None,
+                       block_table=None, new_len=None, status=None) == TA_OK

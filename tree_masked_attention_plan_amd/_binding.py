@@ -5,7 +5,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
-from typing import NamedTuple, Optional
+from typing import NamedTuple, Optional, Tuple
 
 import torch
 
@@ -57,6 +57,9 @@ def load_library():
         getattr(lib, name).argtypes = fwd_args + [P]
     lib.tree_attn_fwd_check.restype = ctypes.c_int
     lib.tree_attn_fwd_check.argtypes = fwd_args
+    lib.tree_attn_commit.restype = ctypes.c_int
+    lib.tree_attn_commit.argtypes = [P, P, P, P, P, P, P, P, P, P,
+                                     i32, i32, i32, i32, i32, i32, i32, i32, ctypes.c_int, P, P, P]
     _lib = lib
     return lib
 
@@ -134,6 +137,51 @@ def plan(parent: torch.Tensor, tree_off: torch.Tensor, prefix_len: torch.Tensor,
                                        _ptr(out.pos_id), _ptr(out.status), _stream(dev, stream))
     _raise(rc, "tree_attn_plan")
     return out
+
+
+def commit(anc_mask: torch.Tensor, depth: torch.Tensor, tree_off: torch.Tensor,
+           prefix_len: torch.Tensor, accepted: torch.Tensor, k_tree: torch.Tensor,
+           v_tree: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_table: torch.Tensor, max_tree: Optional[int] = None, *,
+           new_prefix_len: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
+           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Append each request's accepted path (node ``accepted[b]`` and its
+    ancestors, from :func:`plan`'s ``anc_mask`` / ``depth``) to its paged
+    K/V cache, in place.  Returns ``(new_prefix_len, status)`` (device)."""
+    if k_cache.dtype not in TA_DTYPE:
+        raise ValueError(f"unsupported dtype {k_cache.dtype}")
+    dt = k_cache.dtype
+    for name, t in (("k_tree", k_tree), ("v_tree", v_tree), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, name, dt)
+    _dev_tensor(anc_mask, "anc_mask", torch.int64)
+    for name, t in (("depth", depth), ("tree_off", tree_off), ("prefix_len", prefix_len),
+                    ("accepted", accepted), ("block_table", block_table)):
+        _dev_tensor(t, name, torch.int32)
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or k_tree.dim() != 3 or v_tree.shape != k_tree.shape:
+        raise ValueError("k_cache/v_cache must be [num_pages,page_size,Hkv,D] and k_tree/v_tree [N,Hkv,D]")
+    num_pages, page_size, Hkv, D = k_cache.shape
+    N = k_tree.shape[0]
+    B = prefix_len.numel()
+    if k_tree.shape[1:] != (Hkv, D) or tree_off.numel() != B + 1 or accepted.numel() != B:
+        raise ValueError("inconsistent shapes")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    if anc_mask.shape != (N, MASK_WORDS) or depth.numel() != N:
+        raise ValueError("anc_mask / depth must come from a plan of these trees")
+    if max_tree is None:
+        max_tree = _max_tree_of(tree_off)
+    dev = k_cache.device
+    if new_prefix_len is None:
+        new_prefix_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=dev)
+    rc = load_library().tree_attn_commit(
+        _ptr(anc_mask), _ptr(depth), _ptr(tree_off), _ptr(prefix_len), _ptr(accepted), _ptr(k_tree),
+        _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), B, N, Hkv, D, page_size,
+        num_pages, block_table.shape[1], int(max_tree), TA_DTYPE[dt], _ptr(new_prefix_len),
+        _ptr(status), _stream(dev, stream))
+    _raise(rc, "tree_attn_commit")
+    return new_prefix_len, status
 
 
 def check_status(status: torch.Tensor) -> None:

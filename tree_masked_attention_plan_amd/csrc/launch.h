@@ -42,7 +42,22 @@ struct FwdParams {
     float c2;                       // softmax scale * log2(e)
 };
 
+struct CommitParams {
+    const uint64_t *anc_mask;
+    const int32_t *depth, *tree_off, *prefix_len, *accepted, *block_table;
+    const char *k_tree, *v_tree;
+    char *k_cache, *v_cache;
+    int32_t *new_prefix_len, *status;
+    int32_t B, N, row_bytes, page_shift, num_pages, max_pages, max_tree;
+};
+
+constexpr int kCommitBadAccepted = -3;
+constexpr int kCommitBadPage = -4;
+constexpr int kCommitBadPlan = -5;
+
 hipError_t launch_plan(const PlanParams &p, hipStream_t stream);
+// accepted-path commit: one workgroup per request
+hipError_t launch_commit(const CommitParams &p, hipStream_t stream);
 // nr: 32-row tiles per workgroup of the bf16 kernel; ks: waves per row tile
 // that split each step's keys (see fwd_bf16_kernel)
 hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nr, int ks, hipStream_t stream);

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/tree_attn.h: argument checks,
 // the split-K choice, workspace layout and kernel dispatch.  Every check runs
 // before any HIP call so that bad arguments never reach the device.
+#include <initializer_list>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -225,6 +226,59 @@ ta_status_t tree_attn_plan(const int32_t *parent, const int32_t *tree_off, const
     p.N = N;
     p.max_tree = max_tree;
     return ta::launch_plan(p, (hipStream_t)stream) == hipSuccess ? TA_OK : TA_ERR_HIP;
+}
+
+ta_status_t tree_attn_commit(const uint64_t *anc_mask, const int32_t *depth, const int32_t *tree_off,
+                             const int32_t *prefix_len, const int32_t *accepted, const void *k_tree,
+                             const void *v_tree, void *k_cache, void *v_cache,
+                             const int32_t *block_table, int32_t B, int32_t N, int32_t Hkv, int32_t D,
+                             int32_t page_size, int32_t num_pages, int32_t max_pages_per_seq,
+                             int32_t max_tree, ta_dtype_t dtype, int32_t *new_prefix_len,
+                             int32_t *status, void *stream)
+{
+    if (dtype != TA_DTYPE_BF16 && dtype != TA_DTYPE_FP32)
+        return TA_ERR_UNSUPPORTED;
+    if (max_tree > TREE_ATTN_MAX_TREE || page_size < 1 || page_size > 1024 ||
+        (page_size & (page_size - 1)) != 0)
+        return TA_ERR_UNSUPPORTED;
+    if (B < 0 || N < 0 || Hkv < 1 || D < 1 || max_tree < 0 || num_pages < 0 ||
+        max_pages_per_seq < 0 || (int64_t)N > (int64_t)B * max_tree)
+        return TA_ERR_BAD_SHAPE;
+    const int64_t row_bytes = (int64_t)Hkv * D * (dtype == TA_DTYPE_BF16 ? 2 : 4);
+    if (row_bytes % 16 != 0 || row_bytes > INT32_MAX)
+        return TA_ERR_UNSUPPORTED;
+    if (B == 0)
+        return TA_OK;
+    if (!tree_off || !prefix_len || !accepted || !new_prefix_len || !status || !block_table ||
+        !k_cache || !v_cache)
+        return TA_ERR_NULL_PTR;
+    if (N > 0 && (!anc_mask || !depth || !k_tree || !v_tree))
+        return TA_ERR_NULL_PTR;
+    // rows are copied 16 bytes at a time
+    for (const void *ptr : {k_tree, v_tree, (const void *)k_cache, (const void *)v_cache})
+        if (ptr && ((uintptr_t)ptr & 15) != 0)
+            return TA_ERR_BAD_SHAPE;
+    ta::CommitParams p;
+    p.anc_mask = anc_mask;
+    p.depth = depth;
+    p.tree_off = tree_off;
+    p.prefix_len = prefix_len;
+    p.accepted = accepted;
+    p.block_table = block_table;
+    p.k_tree = (const char *)k_tree;
+    p.v_tree = (const char *)v_tree;
+    p.k_cache = (char *)k_cache;
+    p.v_cache = (char *)v_cache;
+    p.new_prefix_len = new_prefix_len;
+    p.status = status;
+    p.B = B;
+    p.N = N;
+    p.row_bytes = (int32_t)row_bytes;
+    p.page_shift = ilog2(page_size);
+    p.num_pages = num_pages;
+    p.max_pages = max_pages_per_seq;
+    p.max_tree = max_tree;
+    return ta::launch_commit(p, (hipStream_t)stream) == hipSuccess ? TA_OK : TA_ERR_HIP;
 }
 
 int32_t tree_attn_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tree,
