@@ -43,6 +43,8 @@ def _declare(lib):
     lib.oracle_tree_attn.argtypes = [P, P, P, P, P, P, P, P, P,
                                      i32, i32, i32, i32, i32, i32, i32, i32, ctypes.c_double,
                                      P, ctypes.c_int64, P, P, i32]
+    lib.oracle_build_tree.restype = ctypes.c_int
+    lib.oracle_build_tree.argtypes = [P, i32, i32, i32, i32, P, P, P]
     lib.oracle_commit.restype = ctypes.c_int
     lib.oracle_commit.argtypes = [P, P, P, P, P, P, P, P, P,
                                   i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P]
@@ -197,3 +199,19 @@ def commit(parent, tree_off, prefix_len, accepted, k_tree, v_tree, k_cache, v_ca
     if rc != 0:
         raise ValueError(f"oracle_commit: error {rc}")
     return kc, vc, new_len, status
+
+
+def build_tree(logp, T: int):
+    """Best-first draft trees from per-depth candidate log-probabilities
+    ``logp`` [B, Dmax, K] (fp32).  Returns ``(parent, choice, score)``, each
+    [B, T] (int32, int32, float32), nodes in pop order."""
+    lib = _load()
+    lp = _np(logp, np.float32)
+    B, Dmax, K = lp.shape
+    parent = np.zeros((B, T), dtype=np.int32)
+    choice = np.zeros((B, T), dtype=np.int32)
+    score = np.zeros((B, T), dtype=np.float32)
+    rc = lib.oracle_build_tree(_ptr(lp), B, Dmax, K, int(T), _ptr(parent), _ptr(choice), _ptr(score))
+    if rc != 0:
+        raise ValueError(f"oracle_build_tree: error {rc}")
+    return parent, choice, score

@@ -390,3 +390,119 @@ int oracle_commit(const int32_t *parent, const int32_t *tree_off, const int32_t 
     }
     return ORACLE_OK;
 }
+
+/*
+ * Draft-tree construction (JetFlow technical summary, section 2, training
+ * strategy / tree construction: the draft head produces logits for every
+ * tree depth in one pass, a branch score -- by default the cumulative draft
+ * log-probability -- ranks the candidate nodes, and best-first expansion
+ * grows the tree until the token budget is reached).
+ *
+ * Input per request b: logp[b][d][k] (fp32), the log-probability of candidate
+ * token k (0 <= k < K) at depth d + 1 (0 <= d < Dmax), shared by every node at
+ * depth d (the literal reading: one draft distribution per depth).
+ * Best-first, in steps:
+ *   1. a virtual root at depth 0 with score 0 pushes its K children: child k
+ *      has score logp[0][k] and push number k;
+ *   2. T times: pop the candidate with the largest score (equal scores: the
+ *      smaller push number); it becomes node i (i = 0, 1, ... in pop order),
+ *      with parent = the node that pushed it (-1 for the root), choice = its
+ *      k, score = its score; if its depth is below Dmax it pushes its K
+ *      children: child k has score score_i + logp[depth_i][k] (one fp32
+ *      addition) and push number K + K * i + k.
+ * Outputs per request: parent, choice, score for nodes 0 .. T-1 at offset
+ * b * T.  Scores are fp32 sums taken in this order, so any implementation
+ * that adds in the same order decides every comparison identically.
+ * T must not exceed the number of nodes of the implicit tree.
+ */
+typedef struct {
+    float score;
+    int64_t push;
+    int32_t parent, depth, k;
+} cand_t;
+
+static int cand_before(const cand_t *a, const cand_t *b)
+{
+    /* a pops before b */
+    if (a->score != b->score)
+        return a->score > b->score;
+    return a->push < b->push;
+}
+
+static void heap_push(cand_t *h, int64_t *n, cand_t c)
+{
+    int64_t i = (*n)++;
+    h[i] = c;
+    while (i > 0) {
+        int64_t up = (i - 1) / 2;
+        if (!cand_before(&h[i], &h[up]))
+            break;
+        cand_t t = h[i];
+        h[i] = h[up];
+        h[up] = t;
+        i = up;
+    }
+}
+
+static cand_t heap_pop(cand_t *h, int64_t *n)
+{
+    cand_t top = h[0];
+    h[0] = h[--(*n)];
+    int64_t i = 0;
+    for (;;) {
+        int64_t l = 2 * i + 1, r = l + 1, m = i;
+        if (l < *n && cand_before(&h[l], &h[m]))
+            m = l;
+        if (r < *n && cand_before(&h[r], &h[m]))
+            m = r;
+        if (m == i)
+            break;
+        cand_t t = h[i];
+        h[i] = h[m];
+        h[m] = t;
+        i = m;
+    }
+    return top;
+}
+
+int oracle_build_tree(const float *logp, int32_t B, int32_t Dmax, int32_t K, int32_t T,
+                      int32_t *parent, int32_t *choice, float *score)
+{
+    if (B < 0 || Dmax < 1 || K < 1 || T < 0)
+        return ORACLE_ERR_ARGS;
+    /* the implicit tree must hold T nodes */
+    double nodes = 0, level = 1;
+    for (int32_t d = 0; d < Dmax && nodes < T; ++d) {
+        level *= K;
+        nodes += level;
+    }
+    if (nodes < T)
+        return ORACLE_ERR_ARGS;
+    const int64_t cap = (int64_t)K * (T + 1) + 1;
+    cand_t *h = (cand_t *)malloc(sizeof(cand_t) * (size_t)cap);
+    if (!h)
+        return ORACLE_ERR_ALLOC;
+    for (int32_t b = 0; b < B; ++b) {
+        const float *lp = logp + (int64_t)b * Dmax * K;
+        int64_t n = 0;
+        for (int32_t k = 0; k < K; ++k) {
+            cand_t c = {lp[k], k, -1, 1, k};
+            heap_push(h, &n, c);
+        }
+        for (int32_t i = 0; i < T; ++i) {
+            const cand_t c = heap_pop(h, &n);
+            parent[(int64_t)b * T + i] = c.parent;
+            choice[(int64_t)b * T + i] = c.k;
+            score[(int64_t)b * T + i] = c.score;
+            if (c.depth < Dmax) {
+                for (int32_t k = 0; k < K; ++k) {
+                    volatile float s = c.score + lp[(int64_t)c.depth * K + k];
+                    cand_t ch = {s, (int64_t)K + (int64_t)K * i + k, i, c.depth + 1, k};
+                    heap_push(h, &n, ch);
+                }
+            }
+        }
+    }
+    free(h);
+    return ORACLE_OK;
+}

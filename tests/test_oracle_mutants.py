@@ -9,6 +9,7 @@ import pytest
 import oracle
 from tests import test_oracle_commit as commit_pins
 from tests import test_oracle_pins as pins
+from tests import test_oracle_tree as tree_pins
 
 # (description, exact text in tree_attn_oracle.c, replacement).  Mutants run in
 # this process, so none may remove a bounds check (an out-of-bounds write
@@ -42,6 +43,14 @@ MUTANTS = [
      "if (i != a) path[depth++] = i;\n            i = p;"),
     ("commit: V not copied", "memcpy((char *)v_cache + dst_row * row_bytes", "if (0) memcpy((char *)v_cache + dst_row * row_bytes"),
     ("commit: new length not advanced", "new_prefix_len[b] = L + depth;", "new_prefix_len[b] = L;"),
+    ("tree: ties go to the later push", "return a->push < b->push;", "return a->push > b->push;"),
+    ("tree: child score drops the parent's", "volatile float s = c.score + lp[(int64_t)c.depth * K + k];",
+     "volatile float s = lp[(int64_t)c.depth * K + k];"),
+    ("tree: child uses the parent's depth logits", "volatile float s = c.score + lp[(int64_t)c.depth * K + k];",
+     "volatile float s = c.score + lp[(int64_t)(c.depth - 1) * K + k];"),
+    ("tree: depth limit off by one", "if (c.depth < Dmax) {", "if (c.depth < Dmax - 1) {"),
+    ("tree: push numbers per parent collide", "cand_t ch = {s, (int64_t)K + (int64_t)K * i + k, i, c.depth + 1, k};",
+     "cand_t ch = {s, (int64_t)K + k, i, c.depth + 1, k};"),
     ("commit: missing page reported as a bad accepted node", "status[b] = ORACLE_COMMIT_BAD_PAGE;",
      "status[b] = ORACLE_COMMIT_BAD_ACCEPTED;"),
 ]
@@ -62,6 +71,11 @@ PIN_CALLS = [
     commit_pins.test_nothing_accepted_changes_nothing,
     commit_pins.test_two_commits_equal_one_flat_append,
     commit_pins.test_error_statuses_write_nothing_for_that_request,
+    lambda: tree_pins.test_equal_candidates_give_breadth_first_order(3, 12),
+    lambda: tree_pins.test_equal_candidates_give_breadth_first_order(8, 100),
+    tree_pins.test_dominant_candidate_gives_a_chain,
+    lambda: tree_pins.test_top_t_by_brute_force(0),
+    tree_pins.test_structure_invariants,
 ]
 
 
