@@ -175,6 +175,36 @@ ta_status_t tree_attn_fwd(const void *q, const void *k_tree, const void *v_tree,
                           size_t workspace_bytes, void *stream);
 
 /*
+ * tree_attn_build_tree -- best-first draft trees from per-depth candidates.
+ *
+ * The draft head produces logits for every tree depth in one pass; the
+ * cumulative draft log-probability of a branch ranks the candidate nodes,
+ * and best-first expansion grows each request's tree to the token budget
+ * (JetFlow technical summary, section 2, tree construction).
+ *   logp [B, max_depth, K] f32 (device): log-probability of candidate token k
+ *        at depth d + 1, shared by every node at depth d.
+ * Expansion: a virtual root (depth 0, score 0) pushes its K children (child
+ * k: score logp[b, 0, k], push number k).  Then T times: pop the candidate
+ * with the largest score, equal scores going to the smaller push number; it
+ * becomes node i (i = 0, 1, ... in pop order); below max_depth it pushes its
+ * K children, child k with score score_i + logp[b, depth_i, k] (one fp32
+ * addition) and push number K + K*i + k.
+ *   parent [B, T] i32 (device, written): parent node id (-1: hangs off the
+ *          prefix); nodes are in pop order, so parent[i] < i and the trees
+ *          can go to tree_attn_plan with tree_off[b] = b * T.
+ *   choice [B, T] i32: the node's candidate index k at its depth.
+ *   score  [B, T] f32: the node's cumulative log-probability.
+ * Supported: K <= 64, max_depth <= 64, T <= 256, K * (T + 1) <= 16448,
+ *   K * max_depth <= 4096; the implicit tree must hold T nodes
+ *   (TA_ERR_BAD_SHAPE otherwise).  NaN log-probabilities are never chosen;
+ *   if they leave fewer than T candidates, the missing nodes are written with
+ *   parent -1, choice -1 and a NaN score.
+ */
+ta_status_t tree_attn_build_tree(const float *logp, int32_t B, int32_t max_depth, int32_t K,
+                                 int32_t T, int32_t *parent, int32_t *choice, float *score,
+                                 void *stream);
+
+/*
  * tree_attn_commit -- append each request's accepted path to its paged cache.
  *
  * After verification the target model keeps the longest drafted branch it

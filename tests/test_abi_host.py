@@ -230,3 +230,24 @@ def test_commit_empty_batch_is_noop(lib):
     assert commit_call(lib, B=0, N=0, anc=None, depth=None, tree_off=None, prefix_len=None,
                        accepted=None, k_tree=None, v_tree=None, k_cache=None, v_cache=None,
                        block_table=None, new_len=None, status=None) == TA_OK
+
+
+@pytest.mark.parametrize("args,code", [
+    ((2, 16, 65, 16), TA_ERR_UNSUPPORTED),   # K > 64
+    ((2, 65, 8, 16), TA_ERR_UNSUPPORTED),    # depth > 64
+    ((2, 16, 8, 257), TA_ERR_UNSUPPORTED),   # budget > 256
+    ((2, 2, 2, 7), TA_ERR_BAD_SHAPE),        # the implicit tree has 6 nodes
+    ((-1, 16, 8, 16), TA_ERR_BAD_SHAPE),
+    ((2, 16, 0, 16), TA_ERR_BAD_SHAPE),
+])
+def test_build_tree_rejects_before_launch(lib, args, code):
+    B, Dmax, K, T = args
+    f = ctypes.c_void_p(FAKE)
+    assert lib.tree_attn_build_tree(f, B, Dmax, K, T, f, f, f, None) == code
+
+
+def test_build_tree_null_and_empty(lib):
+    f = ctypes.c_void_p(FAKE)
+    assert lib.tree_attn_build_tree(None, 2, 16, 8, 16, f, f, f, None) == TA_ERR_NULL_PTR
+    assert lib.tree_attn_build_tree(None, 0, 16, 8, 16, None, None, None, None) == TA_OK
+    assert lib.tree_attn_build_tree(None, 2, 16, 8, 0, None, None, None, None) == TA_OK

@@ -9,13 +9,14 @@ binding's entry points raises.
     plan(parent, tree_off, prefix_len)   -> anc_mask, depth, pos_id, status
     fwd(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
         tree_off, anc_mask)               -> out, lse
+    build_tree(logp, T)                 -> parent, choice, score
     commit(anc_mask, depth, tree_off, prefix_len, accepted, k_tree, v_tree,
            k_cache, v_cache, block_table)  -> new_prefix_len, status
 """
 from ._binding import (MASK_WORDS, MAX_TREE, FwdCall, PlanResult, TreeAttnError, abi_version,
-                       check_status, commit, fwd, library_path, load_library, num_splits, plan,
+                       build_tree, check_status, commit, fwd, library_path, load_library, num_splits, plan,
                        prepare_fwd, workspace_bytes)
 
 __all__ = ["MASK_WORDS", "MAX_TREE", "FwdCall", "PlanResult", "TreeAttnError", "abi_version",
-           "check_status", "commit", "fwd", "library_path", "load_library", "num_splits", "plan",
+           "build_tree", "check_status", "commit", "fwd", "library_path", "load_library", "num_splits", "plan",
            "prepare_fwd", "workspace_bytes"]

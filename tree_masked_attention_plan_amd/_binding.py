@@ -57,6 +57,8 @@ def load_library():
         getattr(lib, name).argtypes = fwd_args + [P]
     lib.tree_attn_fwd_check.restype = ctypes.c_int
     lib.tree_attn_fwd_check.argtypes = fwd_args
+    lib.tree_attn_build_tree.restype = ctypes.c_int
+    lib.tree_attn_build_tree.argtypes = [P, i32, i32, i32, i32, P, P, P, P]
     lib.tree_attn_commit.restype = ctypes.c_int
     lib.tree_attn_commit.argtypes = [P, P, P, P, P, P, P, P, P, P,
                                      i32, i32, i32, i32, i32, i32, i32, i32, ctypes.c_int, P, P, P]
@@ -137,6 +139,25 @@ def plan(parent: torch.Tensor, tree_off: torch.Tensor, prefix_len: torch.Tensor,
                                        _ptr(out.pos_id), _ptr(out.status), _stream(dev, stream))
     _raise(rc, "tree_attn_plan")
     return out
+
+
+def build_tree(logp: torch.Tensor, T: int, *, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Best-first draft trees of budget ``T`` from per-depth candidate
+    log-probabilities ``logp`` [B, max_depth, K] (fp32).  Returns ``(parent,
+    choice, score)``, each [B, T], nodes in pop order (``parent[b, i] < i``;
+    -1 hangs off the prefix)."""
+    _dev_tensor(logp, "logp", torch.float32)
+    if logp.dim() != 3:
+        raise ValueError("logp must be [B, max_depth, K]")
+    B, Dmax, K = logp.shape
+    dev = logp.device
+    parent = torch.empty((B, T), dtype=torch.int32, device=dev)
+    choice = torch.empty((B, T), dtype=torch.int32, device=dev)
+    score = torch.empty((B, T), dtype=torch.float32, device=dev)
+    rc = load_library().tree_attn_build_tree(_ptr(logp), B, Dmax, K, int(T), _ptr(parent), _ptr(choice),
+                                             _ptr(score), _stream(dev, stream))
+    _raise(rc, "tree_attn_build_tree")
+    return parent, choice, score
 
 
 def commit(anc_mask: torch.Tensor, depth: torch.Tensor, tree_off: torch.Tensor,

@@ -1172,8 +1172,130 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitParams p)
 }
 
 // ---------------------------------------------------------------------------
+// best-first draft trees: one wave per request.  Candidate slot e is the e-th
+// push (the root's children are 0..K-1, node i's children K + K*i .. +K-1),
+// so the slot index is also the tie-break key, the candidate's parent and
+// token follow from it, and a candidate never moves.  Every lane keeps the
+// best of the slots it owns (e % 64 == lane); a pop is a wave-wide argmax of
+// those, after which only the owner of the popped slot rescans, and the K
+// new children land on K distinct lanes.  Scores are the same fp32 sums, in
+// the same order, as in the sequential definition, so every comparison is
+// decided identically.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool cand_better(float sa, int ea, float sb, int eb)
+{
+    return sa > sb || (sa == sb && ea < eb);
+}
+
+__global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p)
+{
+    // candidate scores; NaN marks a slot that is empty or already popped (NaN
+    // never compares better, while -inf is a real score: probability 0)
+    __shared__ float pool[kTreeMaxPool];
+    __shared__ float lps[kTreeMaxLogp];      // this request's log-probabilities
+    __shared__ float node_score[kMaxTree];
+    __shared__ int32_t node_depth[kMaxTree];
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int K = p.K, T = p.T, Dmax = p.Dmax;
+    const int cap = K * (T + 1);
+    const float *lp = p.logp + (int64_t)b * Dmax * K;
+    for (int i = lane; i < Dmax * K; i += 64)
+        lps[i] = lp[i];
+    const float kEmpty = __builtin_nanf("");
+    for (int e = lane; e < cap; e += 64)
+        pool[e] = kEmpty;
+    __syncthreads();
+    // the root's children
+    float best_s = -INFINITY;
+    int best_e = INT32_MAX;
+    if (lane < K) {
+        pool[lane] = lps[lane];
+        best_s = lps[lane];
+        best_e = lane;
+    }
+    __syncthreads();
+    int32_t *out_parent = p.parent + (int64_t)b * T;
+    int32_t *out_choice = p.choice + (int64_t)b * T;
+    float *out_score = p.score + (int64_t)b * T;
+    for (int i = 0; i < T; ++i) {
+        // wave-wide argmax of the lanes' bests (larger score, then smaller slot)
+        float ws = best_s;
+        int we = best_e;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float os = __shfl_xor(ws, o);
+            const int oe = __shfl_xor(we, o);
+            if (cand_better(os, oe, ws, we)) {
+                ws = os;
+                we = oe;
+            }
+        }
+        if (we == INT32_MAX) {
+            // no candidate left: only possible with NaN inputs (the host
+            // checks that the implicit tree holds T nodes); the remaining
+            // nodes are marked as such
+            for (int r = i + lane; r < T; r += 64) {
+                out_parent[r] = -1;
+                out_choice[r] = -1;
+                out_score[r] = kEmpty;
+            }
+            break;
+        }
+        const int e = we;                         // uniform
+        const int par = e < K ? -1 : (e - K) / K;
+        const int k = e < K ? e : (e - K) % K;
+        const int depth = par < 0 ? 1 : node_depth[par] + 1;
+        if (lane == 0) {
+            out_parent[i] = par;
+            out_choice[i] = k;
+            out_score[i] = ws;
+            node_score[i] = ws;
+            node_depth[i] = depth;
+        }
+        // the owner of slot e drops it and finds its next best
+        if (lane == (e & 63)) {
+            pool[e] = kEmpty;
+            best_s = -INFINITY;
+            best_e = INT32_MAX;
+            for (int f = lane; f < cap; f += 64) {
+                const float fs = pool[f];
+                if (cand_better(fs, f, best_s, best_e)) {
+                    best_s = fs;
+                    best_e = f;
+                }
+            }
+        }
+        // node i pushes its K children (slots K + K*i + c)
+        if (depth < Dmax) {
+            const int e0 = K + K * i;
+            for (int c = 0; c < K; ++c) {
+                const int f = e0 + c;
+                if (lane == (f & 63)) {
+                    const float fs = ws + lps[depth * K + c];
+                    pool[f] = fs;
+                    if (cand_better(fs, f, best_s, best_e)) {
+                        best_s = fs;
+                        best_e = f;
+                    }
+                }
+            }
+        }
+        __syncthreads();   // node_depth / pool writes before the next pop reads them
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+hipError_t launch_build_tree(const TreeParams &p, hipStream_t stream)
+{
+    if (p.B == 0 || p.T == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(build_tree_kernel, dim3(p.B), dim3(64), 0, stream, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_commit(const CommitParams &p, hipStream_t stream)
 {
     if (p.B == 0)

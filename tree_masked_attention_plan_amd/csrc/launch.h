@@ -55,7 +55,20 @@ constexpr int kCommitBadAccepted = -3;
 constexpr int kCommitBadPage = -4;
 constexpr int kCommitBadPlan = -5;
 
+struct TreeParams {
+    const float *logp;   // [B, Dmax, K]
+    int32_t *parent, *choice;
+    float *score;        // [B, T] each
+    int32_t B, Dmax, K, T;
+};
+constexpr int kTreeMaxK = 64;          // candidates per depth (one lane each)
+constexpr int kTreeMaxDepth = 64;
+constexpr int kTreeMaxPool = 16448;    // K * (T + 1) candidate slots
+constexpr int kTreeMaxLogp = 4096;     // Dmax * K
+
 hipError_t launch_plan(const PlanParams &p, hipStream_t stream);
+// best-first draft trees: one wave per request
+hipError_t launch_build_tree(const TreeParams &p, hipStream_t stream);
 // accepted-path commit: one workgroup per request
 hipError_t launch_commit(const CommitParams &p, hipStream_t stream);
 // nr: 32-row tiles per workgroup of the bf16 kernel; ks: waves per row tile

@@ -228,6 +228,40 @@ ta_status_t tree_attn_plan(const int32_t *parent, const int32_t *tree_off, const
     return ta::launch_plan(p, (hipStream_t)stream) == hipSuccess ? TA_OK : TA_ERR_HIP;
 }
 
+ta_status_t tree_attn_build_tree(const float *logp, int32_t B, int32_t max_depth, int32_t K,
+                                 int32_t T, int32_t *parent, int32_t *choice, float *score,
+                                 void *stream)
+{
+    if (K > ta::kTreeMaxK || max_depth > ta::kTreeMaxDepth || T > TREE_ATTN_MAX_TREE)
+        return TA_ERR_UNSUPPORTED;
+    if (B < 0 || K < 1 || max_depth < 1 || T < 0)
+        return TA_ERR_BAD_SHAPE;
+    if ((int64_t)K * (T + 1) > ta::kTreeMaxPool || (int64_t)K * max_depth > ta::kTreeMaxLogp)
+        return TA_ERR_UNSUPPORTED;
+    // the implicit tree (K children per node, max_depth levels) must hold T nodes
+    double nodes = 0, level = 1;
+    for (int32_t d = 0; d < max_depth && nodes < T; ++d) {
+        level *= K;
+        nodes += level;
+    }
+    if (nodes < T)
+        return TA_ERR_BAD_SHAPE;
+    if (B == 0 || T == 0)
+        return TA_OK;
+    if (!logp || !parent || !choice || !score)
+        return TA_ERR_NULL_PTR;
+    ta::TreeParams p;
+    p.logp = logp;
+    p.parent = parent;
+    p.choice = choice;
+    p.score = score;
+    p.B = B;
+    p.Dmax = max_depth;
+    p.K = K;
+    p.T = T;
+    return ta::launch_build_tree(p, (hipStream_t)stream) == hipSuccess ? TA_OK : TA_ERR_HIP;
+}
+
 ta_status_t tree_attn_commit(const uint64_t *anc_mask, const int32_t *depth, const int32_t *tree_off,
                              const int32_t *prefix_len, const int32_t *accepted, const void *k_tree,
                              const void *v_tree, void *k_cache, void *v_cache,
