@@ -358,6 +358,52 @@ def summarize_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_
     print(json.dumps(res))
 
 
+def time_calls(fn, reps: int) -> float:
+    """Mean seconds per call of ``fn`` launched back to back on the current
+    stream, from HIP events (after one warm-up call)."""
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
+
+
+def measure_adjacent(dev) -> dict:
+    """The steps next to the attention path, at the budget-256 (moe) shape:
+    best-first draft-tree construction (32 requests, depth 16, 8 candidates
+    per depth, budget 256) and the commit of accepted paths into the paged
+    cache (32 requests, 4 kv heads, head_dim 128)."""
+    rng = np.random.default_rng(2024)
+    z = torch.from_numpy(rng.normal(0.0, 2.0, size=(32, 16, 8)))
+    logp = torch.log_softmax(z, dim=-1).float().to(dev)
+    t_tree = time_calls(lambda: ta.build_tree(logp, 256), 50)
+    parent, _, _ = ta.build_tree(logp, 256)
+    trees = [t.numpy() for t in parent.cpu()]
+    w = W.make_workload("moe-commit", [4096] * 32, trees, 32, 4, 128, torch.bfloat16, 1004,
+                        reserve_tokens=16).to(dev)
+    res = ta.plan(w.parent, w.tree_off, w.prefix_len, max_tree=256)
+    acc_np = W.random_accepted(trees, np.random.default_rng(7), p_none=0.0)
+    acc = torch.from_numpy(acc_np).to(dev)
+    t_commit = time_calls(lambda: ta.commit(res.anc_mask, res.depth, w.tree_off, w.prefix_len, acc,
+                                            w.k_tree, w.v_tree, w.k_cache, w.v_cache, w.block_table,
+                                            max_tree=256), 50)
+    depth = res.depth.cpu().numpy()
+    off = w.tree_off.cpu().numpy()
+    rows = int(sum(depth[off[b] + acc_np[b]] for b in range(32)))
+    moved = rows * 4 * 128 * 2 * 2 * 2      # K and V rows, read once and written once
+    log(f"[bench] draft tree (32 x budget 256): {t_tree * 1e6:.2f} us; commit of {rows} path rows: "
+        f"{t_commit * 1e6:.2f} us ({moved / t_commit / 1e9:.1f} GB/s)")
+    return {"draft_tree": {"us": t_tree * 1e6, "requests": 32, "budget": 256, "max_depth": 16,
+                           "candidates": 8},
+            "commit": {"us": t_commit * 1e6, "requests": 32, "path_rows": rows, "bytes": moved,
+                       "GB/s": moved / t_commit / 1e9}}
+
+
 def calibrate_copy(mib: int, reps: int):
     """A plain device copy of known size, for scaling HBM byte counters."""
     dev = torch.device("cuda:0")
@@ -438,6 +484,8 @@ def main():
                              "roofline": sec["roofline"]}
         if "cpu_baseline" in sec:
             line["budget256"]["cpu_baseline"] = sec["cpu_baseline"]
+    if not args.no_secondary:
+        line["adjacent"] = measure_adjacent(dev)
     print(json.dumps(line), flush=True)
 
 
