@@ -39,7 +39,7 @@ METRIC = "tree-attn tree tokens/s + % bf16 MFMA peak (budget 256) / % HBM BW (bu
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_FP32_TFLOPS = 157.3
-KERNEL_SRC = os.path.join(HERE, "tree_masked_attention_plan_amd", "csrc", "kernels.hip")
+KERNEL_SRC = os.path.join(HERE, "tree_masked_attention_plan_amd", "csrc", "attn.hip")
 PROFILES = os.path.join(HERE, "profiles")
 ROTATE_BYTES = 600 << 20       # cycle at least this much input per pass over replicas
 MAX_REPLICAS = 64
@@ -358,19 +358,29 @@ def summarize_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_
     print(json.dumps(res))
 
 
-def time_calls(fn, reps: int) -> float:
-    """Mean seconds per call of ``fn`` launched back to back on the current
-    stream, from HIP events (after one warm-up call)."""
-    fn()
+def time_calls(fn, reps: int, per_graph: int = 20) -> float:
+    """Mean seconds per call of ``fn``: ``per_graph`` calls captured in one
+    HIP graph, replayed back to back and timed with HIP events on the replay
+    stream (so neither the Python launch path nor the host's graph-launch
+    cost of a microsecond-scale kernel is in the figure)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()                      # eager warm-up before capture
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    g = capture(fn, per_graph)
+    g.replay()
+    torch.cuda.synchronize()
+    n = max(1, reps // per_graph)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(reps):
-        fn()
+    for _ in range(n):
+        g.replay()
     e1.record()
     e1.synchronize()
-    return e0.elapsed_time(e1) / 1e3 / reps
+    return e0.elapsed_time(e1) / 1e3 / (n * per_graph)
 
 
 def measure_adjacent(dev) -> dict:
@@ -381,7 +391,7 @@ def measure_adjacent(dev) -> dict:
     rng = np.random.default_rng(2024)
     z = torch.from_numpy(rng.normal(0.0, 2.0, size=(32, 16, 8)))
     logp = torch.log_softmax(z, dim=-1).float().to(dev)
-    t_tree = time_calls(lambda: ta.build_tree(logp, 256), 50)
+    t_tree = time_calls(lambda: ta.build_tree(logp, 256), 40, per_graph=10)
     parent, _, _ = ta.build_tree(logp, 256)
     trees = [t.numpy() for t in parent.cpu()]
     w = W.make_workload("moe-commit", [4096] * 32, trees, 32, 4, 128, torch.bfloat16, 1004,
@@ -391,7 +401,7 @@ def measure_adjacent(dev) -> dict:
     acc = torch.from_numpy(acc_np).to(dev)
     t_commit = time_calls(lambda: ta.commit(res.anc_mask, res.depth, w.tree_off, w.prefix_len, acc,
                                             w.k_tree, w.v_tree, w.k_cache, w.v_cache, w.block_table,
-                                            max_tree=256), 50)
+                                            max_tree=256), 400)
     depth = res.depth.cpu().numpy()
     off = w.tree_off.cpu().numpy()
     rows = int(sum(depth[off[b] + acc_np[b]] for b in range(32)))

@@ -1,4 +1,4 @@
-// Device code of the tree-causal paged attention library (gfx950 / CDNA4).
+// Device code of tree-causal paged attention (gfx950 / CDNA4).
 //
 // What is computed (JetFlow: Breaking the Scaling Ceiling of Speculative
 // Decoding with Parallel Tree Drafting -- technical summary, section 2, core
@@ -9,13 +9,12 @@
 // Hopper; this file is an independent design for CDNA4).
 //
 // Kernels:
-//   plan_kernel       parent[] -> ancestor bitmask / depth / pos id / status
-//   fwd_bf16_kernel   per (request, kv head, row tile, prefix split): packs the
+//   fwd_bf16_kernel   per (request, kv head, row tile, split slot): packs the
 //                     (node x GQA group) query rows into 32-row MFMA tiles,
 //                     streams 64-key blocks of the paged prefix through LDS,
 //                     then the request's own tree keys under the ancestor
 //                     bitmask, with an online softmax in registers
-//   merge_kernel      LSE merge of prefix splits (split-K)
+//   merge_kernel      LSE merge of the split slots (split-K)
 //   fwd_f32_kernel    fp32 path: one wave per query row, plain FMA arithmetic
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -38,70 +37,6 @@ static constexpr float kLn2 = 0.69314718055994530942f;
 static constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// ---------------------------------------------------------------------------
-// plan: one workgroup per request, one thread per local node (<= 256)
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void plan_kernel(PlanParams p)
-{
-    __shared__ int32_t par[kMaxTree];
-    __shared__ int32_t first_bad;
-    const int b = blockIdx.x;
-    const int j = threadIdx.x;
-    const int32_t off = p.tree_off[b];
-    const int32_t end = p.tree_off[b + 1];
-    const int32_t T = end - off;
-    const int32_t L = p.prefix_len[b];
-    // request-level checks: identical in every thread, so the early return
-    // below is uniform across the workgroup
-    const bool bad_off = (T < 0) || (T > p.max_tree) || (off < 0) || (end > p.N) ||
-                         (b == 0 && off != 0) || (b == p.B - 1 && end != p.N);
-    if (bad_off || L < 0) {
-        if (j == 0)
-            p.status[b] = bad_off ? kTreeBadOffsets : kTreeBadPrefix;
-        return;
-    }
-    if (j == 0)
-        first_bad = INT32_MAX;
-    int32_t pj = -1;
-    if (j < T) {
-        pj = p.parent[off + j];
-        par[j] = pj;
-    }
-    __syncthreads();
-    if (j < T && (pj < -1 || pj >= j))
-        atomicMin(&first_bad, j);
-    __syncthreads();
-    const int32_t fb = first_bad;
-    if (fb != INT32_MAX) {
-        if (j == 0)
-            p.status[b] = fb + 1;
-        return;
-    }
-    if (j < T) {
-        // every parent precedes its child, so the walk ends within j+1 steps
-        uint64_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
-        int32_t d = 0;
-        for (int32_t a = j; a >= 0; a = par[a]) {
-            const uint64_t bit = 1ull << (a & 63);
-            const int word = a >> 6;
-            w0 |= word == 0 ? bit : 0;
-            w1 |= word == 1 ? bit : 0;
-            w2 |= word == 2 ? bit : 0;
-            w3 |= word == 3 ? bit : 0;
-            ++d;
-        }
-        uint64_t *row = p.anc_mask + (int64_t)(off + j) * kMaskWords;
-        row[0] = w0;
-        row[1] = w1;
-        row[2] = w2;
-        row[3] = w3;
-        p.depth[off + j] = d;
-        p.pos_id[off + j] = L + d - 1;
-    }
-    if (j == 0)
-        p.status[b] = kTreeOk;
-}
 
 // ---------------------------------------------------------------------------
 // shared helpers for the forward kernels
@@ -1073,323 +1008,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p)
 }
 
 // ---------------------------------------------------------------------------
-// accepted-path commit: one workgroup per request.  Node j of the request is
-// on the accepted node's root path iff bit j of that node's ancestor mask is
-// set, and it is the token at position L + depth[j] - 1, so the path needs no
-// walk: the workgroup gathers the path's rows by depth, checks every target
-// page, then copies the rows 16 bytes per thread.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void commit_kernel(CommitParams p)
-{
-    __shared__ int32_t src_row[kMaxTree];   // tree row of the path node at depth d + 1
-    __shared__ int64_t dst_row[kMaxTree];   // cache row of position L + d
-    const int b = blockIdx.x;
-    const int j = threadIdx.x;
-    typedef const __attribute__((address_space(4))) int32_t *cint_p;
-    const int32_t off = ((cint_p)p.tree_off)[b];
-    const int32_t end = ((cint_p)p.tree_off)[b + 1];
-    const int32_t T = end - off;
-    const int32_t L = ((cint_p)p.prefix_len)[b];
-    const int32_t a = ((cint_p)p.accepted)[b];
-    // request-level checks, identical in every thread (uniform exits)
-    int st = kTreeOk;
-    if (T < 0 || T > p.max_tree || off < 0 || end > p.N || (b == 0 && off != 0) ||
-        (b == p.B - 1 && end != p.N))
-        st = kTreeBadOffsets;
-    else if (L < 0)
-        st = kTreeBadPrefix;
-    else if (a < -1 || a >= T)
-        st = kCommitBadAccepted;
-    if (st != kTreeOk || a == -1) {
-        if (j == 0) {
-            p.status[b] = st;
-            p.new_prefix_len[b] = L;
-        }
-        return;
-    }
-    const int32_t da = min(max(p.depth[off + a], 0), T);   // path length
-    // the path has one node per depth: as many mask bits as its length
-    int pc = 0;
-#pragma unroll
-    for (int w = 0; w < kMaskWords; ++w)
-        pc += __builtin_popcountll(p.anc_mask[(int64_t)(off + a) * kMaskWords + w]);
-    src_row[j] = -1;
-    __syncthreads();
-    // gather: the path node at depth d + 1 goes to src_row[d]
-    if (j < T) {
-        const uint64_t word = p.anc_mask[(int64_t)(off + a) * kMaskWords + (j >> 6)];
-        if ((word >> (j & 63)) & 1ull) {
-            const int d = p.depth[off + j] - 1;
-            if (d >= 0 && d < da)
-                src_row[d] = off + j;
-        }
-    }
-    __syncthreads();
-    // the plan data must name one node per depth (it does when it comes from a
-    // successful plan of this tree); then every target position needs a page
-    bool incomplete = (j < da && src_row[j] < 0) || pc != da;
-    if (__syncthreads_or(incomplete)) {
-        if (j == 0) {
-            p.status[b] = kCommitBadPlan;
-            p.new_prefix_len[b] = L;
-        }
-        return;
-    }
-    bool bad = false;
-    if (j < da) {
-        const int64_t t = (int64_t)L + j;
-        const int64_t pi = t >> p.page_shift;
-        int32_t page = -1;
-        if (pi < p.max_pages)
-            page = p.block_table[(int64_t)b * p.max_pages + pi];
-        bad = page < 0 || page >= p.num_pages;
-        dst_row[j] = ((int64_t)page << p.page_shift) + (t & ((1 << p.page_shift) - 1));
-    }
-    if (__syncthreads_or(bad)) {
-        if (j == 0) {
-            p.status[b] = kCommitBadPage;
-            p.new_prefix_len[b] = L;
-        }
-        return;
-    }
-    // copy da rows of K and V, 16 bytes per thread per step
-    const int cpr = p.row_bytes >> 4;   // 16-byte chunks per row
-    const int total = da * cpr;
-    for (int c = j; c < total; c += 256) {
-        const int d = c / cpr;
-        const int o = (c - d * cpr) << 4;
-        const int64_t s = (int64_t)src_row[d] * p.row_bytes + o;
-        const int64_t t = dst_row[d] * p.row_bytes + o;
-        const u32x4 kv = *(const u32x4 *)(p.k_tree + s);
-        const u32x4 vv = *(const u32x4 *)(p.v_tree + s);
-        *(u32x4 *)(p.k_cache + t) = kv;
-        *(u32x4 *)(p.v_cache + t) = vv;
-    }
-    if (j == 0) {
-        p.status[b] = kTreeOk;
-        p.new_prefix_len[b] = L + da;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// best-first draft trees: one wave per request.  Candidate slot e is the e-th
-// push (the root's children are 0..K-1, node i's children K + K*i .. +K-1),
-// so the slot index is also the tie-break key, and the candidate's parent and
-// token follow from it.  Slots are grouped in chunks of 64 whose best
-// candidate is kept in LDS (a two-level tournament): a pop is a wave-wide
-// argmax over the chunk bests, and afterwards only the chunks that changed
-// (the popped slot's, and the one or two the new children land in) are
-// re-reduced, one slot per lane.  Scores are the same fp32 sums, in the same
-// order, as in the sequential definition, so every comparison is decided
-// identically.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ bool cand_better(float sa, int ea, float sb, int eb)
-{
-    return sa > sb || (sa == sb && ea < eb);
-}
-
-// A candidate as one 64-bit key whose unsigned order is the pop order:
-// larger score first (the float's bits mapped to an order-preserving
-// unsigned), then smaller slot.  Key 0 is "no candidate" (also NaN scores,
-// which never compare better); -inf is a real score and keys above 0.
-__device__ __forceinline__ uint64_t cand_key(float s, int e)
-{
-    if (e == INT32_MAX || s != s)
-        return 0ull;
-    if (s == 0.f)
-        s = 0.f;   // -0 and +0 are equal scores: one key
-    uint32_t u = __builtin_bit_cast(uint32_t, s);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-
-__device__ __forceinline__ void cand_of_key(uint64_t k, float &s, int &e)
-{
-    if (k == 0ull) {
-        s = -INFINITY;
-        e = INT32_MAX;
-        return;
-    }
-    uint32_t u = (uint32_t)(k >> 32);
-    u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
-    s = __builtin_bit_cast(float, u);
-    e = (int)(0xFFFFFFFFu - (uint32_t)k);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
-{
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)
-{
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// wave-wide best of (s, e) pairs; every lane gets the result.  DPP rotations
-// inside each row of 16 lanes (row_ror 1, 2, 4, 8), then the four row maxima
-// through readlane: a few cycles per step, no LDS round trips.
-__device__ __forceinline__ void wave_best(float &s, int &e)
-{
-    uint64_t k = cand_key(s, e);
-    uint64_t o;
-    o = dpp_u64<0x121>(k); k = o > k ? o : k;   // row_ror:1
-    o = dpp_u64<0x122>(k); k = o > k ? o : k;   // row_ror:2
-    o = dpp_u64<0x124>(k); k = o > k ? o : k;   // row_ror:4
-    o = dpp_u64<0x128>(k); k = o > k ? o : k;   // row_ror:8
-    const uint64_t r0 = readlane_u64(k, 0), r1 = readlane_u64(k, 16);
-    const uint64_t r2 = readlane_u64(k, 32), r3 = readlane_u64(k, 48);
-    const uint64_t a = r0 > r1 ? r0 : r1, c = r2 > r3 ? r2 : r3;
-    cand_of_key(a > c ? a : c, s, e);
-}
-
-__global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p)
-{
-    constexpr int kChunks = (kTreeMaxPool + 63) / 64;
-    // candidate scores; NaN marks a slot that is empty or already popped (NaN
-    // never compares better, while -inf is a real score: probability 0)
-    __shared__ float pool[kTreeMaxPool];
-    __shared__ float cbest_s[kChunks];       // best candidate of each 64-slot chunk
-    __shared__ int32_t cbest_e[kChunks];
-    __shared__ float lps[kTreeMaxLogp];      // this request's log-probabilities
-    __shared__ int32_t node_depth[kMaxTree];
-    // outputs are staged here and written once at the end: a global store in
-    // the loop would make every pop's barrier wait for a memory round trip
-    __shared__ int32_t o_parent[kMaxTree], o_choice[kMaxTree];
-    __shared__ float o_score[kMaxTree];
-    const int b = blockIdx.x;
-    const int lane = threadIdx.x;
-    const int K = p.K, T = p.T, Dmax = p.Dmax;
-    const int cap = K * (T + 1);
-    const int nchunks = (cap + 63) / 64;
-    const float kEmpty = __builtin_nanf("");
-    const float *lp = p.logp + (int64_t)b * Dmax * K;
-    for (int i = lane; i < Dmax * K; i += 64)
-        lps[i] = lp[i];
-    for (int e = lane; e < cap; e += 64)
-        pool[e] = kEmpty;
-    for (int c = lane; c < nchunks; c += 64) {
-        cbest_s[c] = -INFINITY;
-        cbest_e[c] = INT32_MAX;
-    }
-    __syncthreads();
-    // re-reduce chunk c from its slots (one per lane)
-    auto refresh = [&](int c) {
-        const int f = c * 64 + lane;
-        float fs = -INFINITY;
-        int fe = INT32_MAX;
-        if (f < cap) {
-            const float v = pool[f];
-            if (cand_better(v, f, fs, fe)) {
-                fs = v;
-                fe = f;
-            }
-        }
-        wave_best(fs, fe);
-        if (lane == 0) {
-            cbest_s[c] = fs;
-            cbest_e[c] = fe;
-        }
-    };
-    // the root's children
-    if (lane < K)
-        pool[lane] = lps[lane];
-    __syncthreads();
-    refresh(0);
-    if (K > 64)
-        refresh(1);
-    __syncthreads();
-    for (int i = lane; i < T; i += 64) {
-        o_parent[i] = -1;
-        o_choice[i] = -1;
-        o_score[i] = kEmpty;
-    }
-    __syncthreads();
-    for (int i = 0; i < T; ++i) {
-        // argmax over the chunk bests
-        float ws = -INFINITY;
-        int we = INT32_MAX;
-        for (int c = lane; c < nchunks; c += 64) {
-            const float cs = cbest_s[c];
-            const int ce = cbest_e[c];
-            if (cand_better(cs, ce, ws, we)) {
-                ws = cs;
-                we = ce;
-            }
-        }
-        wave_best(ws, we);
-        if (we == INT32_MAX)
-            break;   // no candidate left: only with NaN inputs (the host checks
-                     // that the implicit tree holds T nodes); the remaining
-                     // nodes keep parent -1, choice -1, score NaN
-        const int e = we;                         // uniform
-        const int par = e < K ? -1 : (e - K) / K;
-        const int k = e < K ? e : (e - K) % K;
-        const int depth = par < 0 ? 1 : node_depth[par] + 1;
-        if (lane == 0) {
-            o_parent[i] = par;
-            o_choice[i] = k;
-            o_score[i] = ws;
-            node_depth[i] = depth;
-            pool[e] = kEmpty;
-        }
-        // node i pushes its K children (slots K + K*i + c)
-        const int e0 = K + K * i;
-        const bool push = depth < Dmax;
-        if (push && lane < K)
-            pool[e0 + lane] = ws + lps[depth * K + lane];
-        __syncthreads();
-        const int c_pop = e >> 6;
-        refresh(c_pop);
-        if (push) {
-            const int c0 = e0 >> 6, c1 = (e0 + K - 1) >> 6;
-            if (c0 != c_pop)
-                refresh(c0);
-            if (c1 != c0 && c1 != c_pop)
-                refresh(c1);
-        }
-        __syncthreads();   // chunk bests and node_depth before the next pop reads them
-    }
-    __syncthreads();
-    for (int i = lane; i < T; i += 64) {
-        p.parent[(int64_t)b * T + i] = o_parent[i];
-        p.choice[(int64_t)b * T + i] = o_choice[i];
-        p.score[(int64_t)b * T + i] = o_score[i];
-    }
-}
-
-// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_build_tree(const TreeParams &p, hipStream_t stream)
-{
-    if (p.B == 0 || p.T == 0)
-        return hipSuccess;
-    hipLaunchKernelGGL(build_tree_kernel, dim3(p.B), dim3(64), 0, stream, p);
-    return hipGetLastError();
-}
-
-hipError_t launch_commit(const CommitParams &p, hipStream_t stream)
-{
-    if (p.B == 0)
-        return hipSuccess;
-    hipLaunchKernelGGL(commit_kernel, dim3(p.B), dim3(256), 0, stream, p);
-    return hipGetLastError();
-}
-
-hipError_t launch_plan(const PlanParams &p, hipStream_t stream)
-{
-    if (p.B == 0)
-        return hipSuccess;
-    hipLaunchKernelGGL(plan_kernel, dim3(p.B), dim3(256), 0, stream, p);
-    return hipGetLastError();
-}
-
 template <int D, int NR, int KS>
 static void launch_fwd_bf16_t(const FwdParams &p, hipStream_t stream)
 {

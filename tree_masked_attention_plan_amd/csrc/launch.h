@@ -1,5 +1,6 @@
 // Internal interface between the host dispatch (tree_attn.cpp) and the
-// device code (kernels.hip).  Not part of the public ABI.
+// device code (attn.hip, plan.hip, tree.hip, commit.hip).  Not part of the
+// public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
