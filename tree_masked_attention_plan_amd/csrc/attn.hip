@@ -833,25 +833,36 @@ __global__ __launch_bounds__(256) void merge_kernel(FwdParams p)
     constexpr int LPS = D / 4;        // lanes per split row
     constexpr int SPI = 64 / LPS;     // splits per wave-wide load
     constexpr int BATCH = 16;         // loads in flight per lane
+    // the few arguments used, loaded together (opaque copies, as load_args)
+    const float *ws_o = p.ws_o, *ws_lse = p.ws_lse;
+    void *out = p.out;
+    float *lse_out = p.lse;
+    int N = p.N, Hq = p.Hq, ns = p.nsplit;
+    asm volatile("" : "+s"(ws_o), "+s"(ws_lse), "+s"(out), "+s"(lse_out), "+s"(N), "+s"(Hq), "+s"(ns));
     const int lane = threadIdx.x & 63;
     const int64_t r0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // n * Hq + qh
-    if (r0 >= (int64_t)p.N * p.Hq)
+    if (r0 >= (int64_t)N * Hq)
         return;
-    const int ns = p.nsplit;
-    const int64_t split_stride = (int64_t)p.N * p.Hq;   // rows between splits
+    const int64_t split_stride = (int64_t)N * Hq;   // rows between splits
     const int grp = lane / LPS;       // which split of a load this lane takes
     const int dcol = (lane % LPS) * 4;
-    const float *src = p.ws_o + r0 * D + dcol;
+    const float *src = ws_o + r0 * D + dcol;
 
+    // The whole first batch and the lse are in flight before anything waits:
+    // partial rows first, the lse last (vmcnt counts in issue order).  Loads
+    // are unconditional, of a clamped slot, so that no branch separates them;
+    // a slot past the end is dropped by the weighting below.
+    auto load = [&](int s) {
+        return *(const __attribute__((address_space(1))) f32x4 *)(src + min(s, ns - 1) * split_stride * D);
+    };
+    f32x4 v[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i)
+        v[i] = load(i * SPI + grp);
     float ls = -INFINITY;
     if (lane < ns)
-        ls = p.ws_lse[lane * split_stride + r0];
-    float4 v[BATCH];
-#pragma unroll
-    for (int i = 0; i < BATCH; ++i) {
-        const int s = i * SPI + grp;
-        v[i] = s < ns ? *(const float4 *)(src + s * split_stride * D) : float4{0.f, 0.f, 0.f, 0.f};
-    }
+        ls = gmem(ws_lse)[lane * split_stride + r0];
+    __builtin_amdgcn_sched_barrier(0);
     float mx = ls;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
@@ -864,7 +875,7 @@ __global__ __launch_bounds__(256) void merge_kernel(FwdParams p)
         tot += __shfl_xor(tot, o);
 
     float4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto add = [&](const float4 &x, int s) {
+    auto add = [&](const f32x4 &x, int s) {
         const float ws = __shfl(wgt, s & 63);
         if (s < ns && ws > 0.f) {
             acc.x += ws * x.x;
@@ -878,10 +889,8 @@ __global__ __launch_bounds__(256) void merge_kernel(FwdParams p)
         add(v[i], i * SPI + grp);
     for (int s0 = BATCH * SPI; s0 < ns; s0 += BATCH * SPI) {
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            const int s = s0 + i * SPI + grp;
-            v[i] = s < ns ? *(const float4 *)(src + s * split_stride * D) : float4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int i = 0; i < BATCH; ++i)
+            v[i] = load(s0 + i * SPI + grp);
 #pragma unroll
         for (int i = 0; i < BATCH; ++i)
             add(v[i], s0 + i * SPI + grp);
@@ -895,14 +904,14 @@ __global__ __launch_bounds__(256) void merge_kernel(FwdParams p)
     }
     if (grp == 0) {
         const float inv = tot > 0.f ? 1.0f / tot : 0.f;
-        OutT *dst = (OutT *)p.out + r0 * D + dcol;
+        __attribute__((address_space(1))) OutT *dst = gmem((OutT *)out) + r0 * D + dcol;
         dst[0] = (OutT)(acc.x * inv);
         dst[1] = (OutT)(acc.y * inv);
         dst[2] = (OutT)(acc.z * inv);
         dst[3] = (OutT)(acc.w * inv);
     }
     if (lane == 0)
-        p.lse[r0] = tot > 0.f ? (base + __builtin_log2f(tot)) * kLn2 : -INFINITY;
+        gmem(lse_out)[r0] = tot > 0.f ? (base + __builtin_log2f(tot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------

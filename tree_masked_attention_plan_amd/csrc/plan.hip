@@ -11,30 +11,46 @@ namespace ta {
 // ---------------------------------------------------------------------------
 // plan: one workgroup per request, one thread per local node (<= 256)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void plan_kernel(PlanParams p)
+// The argument block is copied into scalar registers in one go: the empty asm
+// makes the copies opaque, so the compiler neither reloads a field where it
+// is first used nor chains those loads behind the first global reads.
+// Accesses through the copies name the global address space explicitly.
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T *gmem(T *ptr)
 {
+    return (__attribute__((address_space(1))) T *)ptr;
+}
+
+__global__ __launch_bounds__(256) void plan_kernel(PlanParams p_arg)
+{
+    PlanParams p = p_arg;
+    asm volatile("" : "+s"(p.parent), "+s"(p.tree_off), "+s"(p.prefix_len), "+s"(p.anc_mask),
+                      "+s"(p.depth), "+s"(p.pos_id), "+s"(p.status), "+s"(p.B), "+s"(p.N),
+                      "+s"(p.max_tree));
     __shared__ int32_t par[kMaxTree];
     __shared__ int32_t first_bad;
     const int b = blockIdx.x;
     const int j = threadIdx.x;
-    const int32_t off = p.tree_off[b];
-    const int32_t end = p.tree_off[b + 1];
+    // both request reads in flight before either is waited for
+    const int32_t L = gmem(p.prefix_len)[b];
+    const int32_t off = gmem(p.tree_off)[b];
+    const int32_t end = gmem(p.tree_off)[b + 1];
+    __builtin_amdgcn_sched_barrier(0);
     const int32_t T = end - off;
-    const int32_t L = p.prefix_len[b];
     // request-level checks: identical in every thread, so the early return
     // below is uniform across the workgroup
     const bool bad_off = (T < 0) || (T > p.max_tree) || (off < 0) || (end > p.N) ||
                          (b == 0 && off != 0) || (b == p.B - 1 && end != p.N);
     if (bad_off || L < 0) {
         if (j == 0)
-            p.status[b] = bad_off ? kTreeBadOffsets : kTreeBadPrefix;
+            gmem(p.status)[b] = bad_off ? kTreeBadOffsets : kTreeBadPrefix;
         return;
     }
     if (j == 0)
         first_bad = INT32_MAX;
     int32_t pj = -1;
     if (j < T) {
-        pj = p.parent[off + j];
+        pj = gmem(p.parent)[off + j];
         par[j] = pj;
     }
     __syncthreads();
@@ -44,7 +60,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p)
     const int32_t fb = first_bad;
     if (fb != INT32_MAX) {
         if (j == 0)
-            p.status[b] = fb + 1;
+            gmem(p.status)[b] = fb + 1;
         return;
     }
     if (j < T) {
@@ -60,16 +76,16 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p)
             w3 |= word == 3 ? bit : 0;
             ++d;
         }
-        uint64_t *row = p.anc_mask + (int64_t)(off + j) * kMaskWords;
+        __attribute__((address_space(1))) uint64_t *row = gmem(p.anc_mask) + (int64_t)(off + j) * kMaskWords;
         row[0] = w0;
         row[1] = w1;
         row[2] = w2;
         row[3] = w3;
-        p.depth[off + j] = d;
-        p.pos_id[off + j] = L + d - 1;
+        gmem(p.depth)[off + j] = d;
+        gmem(p.pos_id)[off + j] = L + d - 1;
     }
     if (j == 0)
-        p.status[b] = kTreeOk;
+        gmem(p.status)[b] = kTreeOk;
 }
 
 // ---------------------------------------------------------------------------
