@@ -551,6 +551,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
             TA_WAIT_VMCNT(0);
         }
         __builtin_amdgcn_s_barrier();           // ... and every other wave's too
+        asm volatile("" ::: "memory");          // no LDS read moves above it
         const int k = j * KSB + my_blk;
         if (k < n_blocks) {
             bool is_tree;
@@ -685,7 +686,9 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
             }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS reads are done
+        asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();         // the stage may now be overwritten
+        asm volatile("" ::: "memory");
     };
 
     // Q and mask words are in registers before the loop: the compiler,
