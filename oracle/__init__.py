@@ -4,7 +4,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
 its Python binding) never imports, links or calls it.
 
-``oracle_tree_attn`` / ``oracle_plan`` live in ``tree_attn_oracle.c`` (plain
+``oracle_tree_attn`` / ``oracle_plan`` / ``oracle_dfs_order`` (and the
+adjacent steps) live in ``tree_attn_oracle.c`` (plain
 C, built with gcc by :func:`build`); this module only marshals numpy arrays.
 """
 from __future__ import annotations
@@ -43,6 +44,8 @@ def _declare(lib):
     lib.oracle_tree_attn.argtypes = [P, P, P, P, P, P, P, P, P,
                                      i32, i32, i32, i32, i32, i32, i32, i32, ctypes.c_double,
                                      P, ctypes.c_int64, P, P, i32]
+    lib.oracle_dfs_order.restype = ctypes.c_int
+    lib.oracle_dfs_order.argtypes = [P, P, P, i32, i32, i32, P, P, P, P]
     lib.oracle_build_tree.restype = ctypes.c_int
     lib.oracle_build_tree.argtypes = [P, i32, i32, i32, i32, P, P, P]
     lib.oracle_commit.restype = ctypes.c_int
@@ -104,6 +107,27 @@ def plan(parent, tree_off, prefix_len, max_tree: int) -> Tuple[np.ndarray, np.nd
     if rc != 0:
         raise ValueError(f"oracle_plan: error {rc}")
     return mask, depth, pos, status
+
+
+def dfs_order(parent, tree_off, prefix_len, max_tree: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Depth-first relabelling of every request's tree (``oracle_dfs_order``):
+    (perm [N] new -> old, inv [N] old -> new, both global node indices;
+    parent_new [N] local parents in the new labelling; status [B])."""
+    lib = _load()
+    parent = _np(parent, np.int32)
+    tree_off = _np(tree_off, np.int32)
+    prefix_len = _np(prefix_len, np.int32)
+    B = len(prefix_len)
+    N = len(parent)
+    perm = np.zeros(N, dtype=np.int32)
+    inv = np.zeros(N, dtype=np.int32)
+    parent_new = np.zeros(N, dtype=np.int32)
+    status = np.zeros(B, dtype=np.int32)
+    rc = lib.oracle_dfs_order(_ptr(parent), _ptr(tree_off), _ptr(prefix_len), B, N, int(max_tree),
+                              _ptr(perm), _ptr(inv), _ptr(parent_new), _ptr(status))
+    if rc != 0:
+        raise ValueError(f"oracle_dfs_order: error {rc}")
+    return perm, inv, parent_new, status
 
 
 def tree_attn(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, tree_off, parent,

@@ -114,6 +114,82 @@ int oracle_plan(const int32_t *parent, const int32_t *tree_off, const int32_t *p
     return ORACLE_OK;
 }
 
+/*
+ * Depth-first relabelling of every request's tree (the pages define only the
+ * mask, JetFlow technical summary, section 2: a node sees its own root path;
+ * any relabelling that keeps parents before children leaves every node's
+ * output unchanged).  The order is the preorder of the forest with the roots,
+ * and each node's children, taken in increasing local index, written with an
+ * explicit stack:
+ *   perm[off + i'] = off + i   (new local index i' of old node i)
+ *   inv[off + i]   = off + i'
+ *   parent_new[off + i'] = new index of parent(i), or -1 for a root.
+ * The status is the plan's (same checks, same codes).  Rows of requests with
+ * a non-zero status get the identity and their parent array unchanged.
+ */
+int oracle_dfs_order(const int32_t *parent, const int32_t *tree_off, const int32_t *prefix_len,
+                     int32_t B, int32_t N, int32_t max_tree,
+                     int32_t *perm, int32_t *inv, int32_t *parent_new, int32_t *status)
+{
+    if (B < 0 || N < 0 || max_tree < 0 || max_tree > ORACLE_MAX_TREE)
+        return ORACLE_ERR_ARGS;
+    for (int32_t n = 0; n < N; ++n) {
+        perm[n] = n;
+        inv[n] = n;
+        parent_new[n] = parent[n];
+    }
+    int32_t stack[ORACLE_MAX_TREE];
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t off = tree_off[b], end = tree_off[b + 1];
+        int32_t T = end - off;
+        int bad_offsets = (T < 0) || (T > max_tree) || (off < 0) || (end > N) ||
+                          (b == 0 && off != 0) || (b == B - 1 && end != N);
+        if (bad_offsets) {
+            status[b] = ORACLE_TREE_BAD_OFFSETS;
+            continue;
+        }
+        if (prefix_len[b] < 0) {
+            status[b] = ORACLE_TREE_BAD_PREFIX;
+            continue;
+        }
+        int32_t first_bad = -1;
+        for (int32_t i = 0; i < T; ++i) {
+            int32_t p = parent[off + i];
+            if (p < -1 || p >= i) {
+                first_bad = i;
+                break;
+            }
+        }
+        if (first_bad >= 0) {
+            status[b] = first_bad + 1;
+            continue;
+        }
+        /* Depth-first walk.  The stack holds nodes still to visit; the
+         * children of a node (and the roots) are pushed largest index first,
+         * so that they come off in increasing index order.  Every node is
+         * pushed exactly once, by its parent (or as a root). */
+        int32_t top = 0, next = 0;
+        for (int32_t i = T - 1; i >= 0; --i)
+            if (parent[off + i] == -1)
+                stack[top++] = i;
+        while (top > 0) {
+            int32_t v = stack[--top];
+            perm[off + next] = off + v;
+            inv[off + v] = off + next;
+            next += 1;
+            for (int32_t c = T - 1; c > v; --c)
+                if (parent[off + c] == v)
+                    stack[top++] = c;
+        }
+        for (int32_t i = 0; i < T; ++i) {
+            int32_t p = parent[off + i];
+            parent_new[inv[off + i]] = (p == -1) ? -1 : inv[off + p] - off;
+        }
+        status[b] = ORACLE_TREE_OK;
+    }
+    return ORACLE_OK;
+}
+
 typedef struct {
     const double *q, *k_tree, *v_tree, *k_cache, *v_cache;
     const int32_t *block_table, *prefix_len, *tree_off, *parent;

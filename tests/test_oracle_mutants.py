@@ -8,6 +8,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_commit as commit_pins
+from tests import test_oracle_dfs as dfs_pins
 from tests import test_oracle_pins as pins
 from tests import test_oracle_tree as tree_pins
 
@@ -53,6 +54,14 @@ MUTANTS = [
      "cand_t ch = {s, (int64_t)K + k, i, c.depth + 1, k};"),
     ("commit: missing page reported as a bad accepted node", "status[b] = ORACLE_COMMIT_BAD_PAGE;",
      "status[b] = ORACLE_COMMIT_BAD_ACCEPTED;"),
+    ("dfs: children taken in decreasing index", "for (int32_t c = T - 1; c > v; --c)\n                if (parent[off + c] == v)",
+     "for (int32_t c = v + 1; c < T; ++c)\n                if (parent[off + c] == v)"),
+    ("dfs: roots taken in decreasing index", "for (int32_t i = T - 1; i >= 0; --i)\n            if (parent[off + i] == -1)",
+     "for (int32_t i = 0; i < T; ++i)\n            if (parent[off + i] == -1)"),
+    ("dfs: parents left in the old labelling", "parent_new[inv[off + i]] = (p == -1) ? -1 : inv[off + p] - off;",
+     "parent_new[inv[off + i]] = p;"),
+    ("dfs: breadth-first instead of depth-first", "int32_t v = stack[--top];",
+     "int32_t v = stack[0]; for (int32_t q = 1; q < top; ++q) stack[q - 1] = stack[q]; --top;"),
 ]
 
 PIN_CALLS = [
@@ -76,6 +85,9 @@ PIN_CALLS = [
     tree_pins.test_dominant_candidate_gives_a_chain,
     lambda: tree_pins.test_top_t_by_brute_force(0),
     tree_pins.test_structure_invariants,
+    lambda: dfs_pins.test_permutation_is_the_lexicographic_order_of_paths(0),
+    dfs_pins.test_hand_written_preorder,
+    lambda: dfs_pins.test_relabelled_tree_is_topological_with_contiguous_subtrees(1),
 ]
 
 
