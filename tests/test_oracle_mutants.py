@@ -34,7 +34,10 @@ MUTANTS = [
     ("max not subtracted in the weights", "double w = exp(score[k] - m) / l;", "double w = exp(score[k]) / l;"),
     ("position id off by one", "pos_id[off + i] = prefix_len[b] + d - 1;", "pos_id[off + i] = prefix_len[b] + d;"),
     ("mask bit shifted", "|= (uint64_t)1 << (j % 64);", "|= (uint64_t)1 << ((j + 1) % 64);"),
-    ("status index not one-based", "status[b] = first_bad + 1;", "status[b] = first_bad;"),
+    ("status index not one-based", "status[b] = first_bad + 1;\n            continue;\n        }\n        for (int32_t i = 0; i < T; ++i) {\n            int32_t d = 0;",
+     "status[b] = first_bad;\n            continue;\n        }\n        for (int32_t i = 0; i < T; ++i) {\n            int32_t d = 0;"),
+    ("dfs: status index not one-based", "status[b] = first_bad + 1;\n            continue;\n        }\n        /* Depth-first walk.",
+     "status[b] = first_bad;\n            continue;\n        }\n        /* Depth-first walk."),
     ("q row of the wrong head", "const double *qrow = J->q + ((int64_t)node * J->Hq + h) * D;",
      "const double *qrow = J->q + ((int64_t)node * J->Hq + (h + 1) % J->Hq) * D;"),
     ("commit: path written leaf first", "const int32_t node = path[depth - d];", "const int32_t node = path[d - 1];"),
@@ -87,6 +90,7 @@ PIN_CALLS = [
     tree_pins.test_structure_invariants,
     lambda: dfs_pins.test_permutation_is_the_lexicographic_order_of_paths(0),
     dfs_pins.test_hand_written_preorder,
+    lambda: dfs_pins.test_bad_trees_report_the_plan_status([-1, 0, 2, 1], 3),
     lambda: dfs_pins.test_relabelled_tree_is_topological_with_contiguous_subtrees(1),
 ]
 
