@@ -414,6 +414,65 @@ def measure_adjacent(dev) -> dict:
                        "GB/s": moved / t_commit / 1e9}}
 
 
+def tree_blocks_visited(anc_mask: np.ndarray, tree_off: np.ndarray, G: int, rows_per_wg: int) -> int:
+    """(workgroup, 64-key tree block) pairs the attention kernel visits: a
+    workgroup's rows cover rows_per_wg / G consecutive nodes, and it copies
+    and computes a tree block when any of its nodes sees a key in it."""
+    words = anc_mask.view(np.uint64)
+    total = 0
+    per = max(1, rows_per_wg // G)
+    for b in range(len(tree_off) - 1):
+        lo, hi = int(tree_off[b]), int(tree_off[b + 1])
+        for s in range(lo, hi, per):
+            total += int(np.count_nonzero(np.bitwise_or.reduce(words[s:min(s + per, hi)], axis=0)))
+    return total
+
+
+def measure_dfs(dev) -> dict:
+    """Depth-first relabelling at budget 256 (tree256 and moe shapes): the
+    attention call on best-first labels against the same call on the
+    relabelled tree (inputs gathered once, outside the timing), with the
+    tree blocks each visits, and the cost of tree_attn_plan_dfs itself
+    against tree_attn_plan.  Same inputs call after call (warm caches): a
+    relative figure."""
+    out = {}
+    for name in ("tree256", "moe"):
+        w_host = W.make_config(name)
+        mt, mp = w_host.max_tree, w_host.max_prefix
+        w = w_host.to(dev)
+        res = ta.plan(w.parent, w.tree_off, w.prefix_len, max_tree=mt)
+        r = ta.plan_dfs(w.parent, w.tree_off, w.prefix_len, max_tree=mt)
+        ta.check_status(res.status)
+        ta.check_status(r.plan.status)
+        q, kt, vt = (ta.gather_rows(t, r.perm) for t in (w.q, w.k_tree, w.v_tree))
+        call_a = ta.prepare_fwd(w.q, w.k_tree, w.v_tree, w.k_cache, w.v_cache, w.block_table, w.prefix_len,
+                                w.tree_off, res.anc_mask, max_tree=mt, max_prefix=mp)
+        call_b = ta.prepare_fwd(q, kt, vt, w.k_cache, w.v_cache, w.block_table, w.prefix_len,
+                                w.tree_off, r.plan.anc_mask, max_tree=mt, max_prefix=mp)
+        reps, per = (100, 20) if name == "tree256" else (48, 4)
+        t_a = time_calls(call_a.run, reps, per_graph=per)
+        t_b = time_calls(call_b.run, reps, per_graph=per)
+        t_plan = time_calls(lambda: ta.plan(w.parent, w.tree_off, w.prefix_len, max_tree=mt,
+                                            out=res), 200)
+        t_dfs = time_calls(lambda: ta.plan_dfs(w.parent, w.tree_off, w.prefix_len, max_tree=mt), 200)
+        torch.cuda.synchronize()
+        off = w.tree_off.cpu().numpy()
+        G = w.Hq // w.Hkv
+        geo = ta.num_splits(w.B, w.Hq, w.Hkv, w.D, mt, mp)
+        rows_wg = 256        # 8 row tiles of 32 query rows per workgroup at these shapes
+        vis_a = tree_blocks_visited(res.anc_mask.cpu().numpy(), off, G, rows_wg)
+        vis_b = tree_blocks_visited(r.plan.anc_mask.cpu().numpy(), off, G, rows_wg)
+        log(f"[bench] {name} attention: best-first labels {t_a * 1e6:.2f} us ({vis_a} tree blocks), "
+            f"depth-first {t_b * 1e6:.2f} us ({vis_b}); plan {t_plan * 1e6:.2f} us, "
+            f"plan_dfs {t_dfs * 1e6:.2f} us (splits {geo})")
+        out[name] = {"attn_us_best_first": t_a * 1e6, "attn_us_depth_first": t_b * 1e6,
+                     "tree_blocks_best_first": vis_a, "tree_blocks_depth_first": vis_b,
+                     "plan_us": t_plan * 1e6, "plan_dfs_us": t_dfs * 1e6}
+        del w, w_host, q, kt, vt, call_a, call_b
+        torch.cuda.empty_cache()
+    return out
+
+
 def calibrate_copy(mib: int, reps: int):
     """A plain device copy of known size, for scaling HBM byte counters."""
     dev = torch.device("cuda:0")
@@ -496,6 +555,7 @@ def main():
             line["budget256"]["cpu_baseline"] = sec["cpu_baseline"]
     if not args.no_secondary:
         line["adjacent"] = measure_adjacent(dev)
+        line["adjacent"]["depth_first_relabel"] = measure_dfs(dev)
     print(json.dumps(line), flush=True)
 
 

@@ -175,6 +175,49 @@ ta_status_t tree_attn_fwd(const void *q, const void *k_tree, const void *v_tree,
                           size_t workspace_bytes, void *stream);
 
 /*
+ * tree_attn_plan_dfs -- the plan, in a depth-first relabelling of each tree.
+ *
+ * The mask (JetFlow technical summary, section 2, tree-causal attention
+ * mask) depends only on each node's root path, so any relabelling that
+ * keeps parents before children changes no node's output.  This entry
+ * relabels each request's forest in preorder, with the roots and each
+ * node's children taken in increasing local index.  A node's ancestors then
+ * sit just before it and every subtree is one contiguous range, so the
+ * ancestor bits of neighbouring rows share 64-key blocks and more tree
+ * blocks are skipped by tree_attn_fwd.
+ *   parent, tree_off, prefix_len, B, N, max_tree: as tree_attn_plan.
+ *   perm     [N] i32 (device, written): perm[off_b + i'] = off_b + i, the old
+ *            global index of the node whose new local index is i'.
+ *   inv_perm [N] i32: inv_perm[off_b + i] = off_b + i' (the inverse).
+ *   parent_new [N] i32: the local parent of every node in the new labelling
+ *            (parent_new[i'] < i').
+ *   anc_mask, depth, pos_id, status: what tree_attn_plan writes for the
+ *            relabelled tree (rows in the new order); the same status codes.
+ * To run the attention in the new order, gather the rows of q, k_tree and
+ * v_tree with perm (tree_attn_gather_rows) and call tree_attn_fwd with this
+ * anc_mask; gathering its out and lse rows with inv_perm restores the old
+ * order.  Outputs of a request with a non-zero status are undefined.
+ * Errors, async behaviour and argument checks: as tree_attn_plan.
+ */
+ta_status_t tree_attn_plan_dfs(const int32_t *parent, const int32_t *tree_off,
+                               const int32_t *prefix_len, int32_t B, int32_t N,
+                               int32_t max_tree, int32_t *perm, int32_t *inv_perm,
+                               int32_t *parent_new, uint64_t *anc_mask, int32_t *depth,
+                               int32_t *pos_id, int32_t *status, void *stream);
+
+/*
+ * tree_attn_gather_rows -- dst[i] = src[index[i]] for n_rows rows of
+ * row_bytes bytes each (device pointers).  It moves the rows of q, k_tree,
+ * v_tree, out or lse between the old and the depth-first labelling of
+ * tree_attn_plan_dfs.  An index outside [0, n_src) yields a zero row.
+ * row_bytes must be a multiple of 4 and src, dst 4-byte aligned
+ * (TA_ERR_BAD_SHAPE / TA_ERR_UNSUPPORTED).  src and dst must not overlap.
+ * Enqueued on stream; returns without synchronising.
+ */
+ta_status_t tree_attn_gather_rows(const void *src, int64_t n_src, const int32_t *index, void *dst,
+                                  int64_t n_rows, int64_t row_bytes, void *stream);
+
+/*
  * tree_attn_build_tree -- best-first draft trees from per-depth candidates.
  *
  * The draft head produces logits for every tree depth in one pass; the

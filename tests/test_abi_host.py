@@ -37,7 +37,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("tree_attn_plan", "tree_attn_fwd", "tree_attn_workspace_bytes",
+    for required in ("tree_attn_plan", "tree_attn_plan_dfs", "tree_attn_gather_rows", "tree_attn_fwd",
+                     "tree_attn_workspace_bytes",
                      "tree_attn_num_splits", "tree_attn_fwd_check", "tree_attn_status_str",
                      "tree_attn_abi_version"):
         assert required in names
@@ -251,3 +252,42 @@ def test_build_tree_null_and_empty(lib):
     assert lib.tree_attn_build_tree(None, 2, 16, 8, 16, f, f, f, None) == TA_ERR_NULL_PTR
     assert lib.tree_attn_build_tree(None, 0, 16, 8, 16, None, None, None, None) == TA_OK
     assert lib.tree_attn_build_tree(None, 2, 16, 8, 0, None, None, None, None) == TA_OK
+
+
+def plan_dfs_call(lib, **over):
+    a = dict(parent=FAKE, tree_off=FAKE, prefix_len=FAKE, B=2, N=300, max_tree=256, perm=FAKE,
+             inv=FAKE, parent_new=FAKE, anc=FAKE, depth=FAKE, pos=FAKE, status=FAKE)
+    a.update(over)
+    P = ctypes.c_void_p
+    return lib.tree_attn_plan_dfs(P(a["parent"]), P(a["tree_off"]), P(a["prefix_len"]), a["B"], a["N"],
+                                  a["max_tree"], P(a["perm"]), P(a["inv"]), P(a["parent_new"]),
+                                  P(a["anc"]), P(a["depth"]), P(a["pos"]), P(a["status"]), None)
+
+
+def test_plan_dfs_argument_checks(lib):
+    assert plan_dfs_call(lib, max_tree=257) == TA_ERR_UNSUPPORTED
+    assert plan_dfs_call(lib, N=513) == TA_ERR_BAD_SHAPE          # more nodes than B * max_tree
+    assert plan_dfs_call(lib, B=-1) == TA_ERR_BAD_SHAPE
+    assert plan_dfs_call(lib, B=0, N=0) == TA_OK                    # nothing to do, nothing launched
+    for name in ("tree_off", "prefix_len", "status", "parent", "perm", "inv", "parent_new", "anc",
+                 "depth", "pos"):
+        assert plan_dfs_call(lib, **{name: 0}) == TA_ERR_NULL_PTR, name
+
+
+def gather_call(lib, **over):
+    a = dict(src=FAKE, n_src=10, index=FAKE, dst=FAKE, n_rows=10, row_bytes=256)
+    a.update(over)
+    P = ctypes.c_void_p
+    return lib.tree_attn_gather_rows(P(a["src"]), a["n_src"], P(a["index"]), P(a["dst"]), a["n_rows"],
+                                     a["row_bytes"], None)
+
+
+def test_gather_rows_argument_checks(lib):
+    assert gather_call(lib, row_bytes=6) == TA_ERR_BAD_SHAPE        # not a multiple of 4
+    assert gather_call(lib, n_rows=-1) == TA_ERR_BAD_SHAPE
+    assert gather_call(lib, n_src=1 << 40) == TA_ERR_BAD_SHAPE      # indices are int32
+    assert gather_call(lib, n_rows=0) == TA_OK                       # nothing to do, nothing launched
+    assert gather_call(lib, index=0) == TA_ERR_NULL_PTR
+    assert gather_call(lib, dst=0) == TA_ERR_NULL_PTR
+    assert gather_call(lib, src=0) == TA_ERR_NULL_PTR
+    assert gather_call(lib, src=FAKE + 2) == TA_ERR_UNSUPPORTED       # not 4-byte aligned

@@ -12,11 +12,13 @@ binding's entry points raises.
     build_tree(logp, T)                 -> parent, choice, score
     commit(anc_mask, depth, tree_off, prefix_len, accepted, k_tree, v_tree,
            k_cache, v_cache, block_table)  -> new_prefix_len, status
+    plan_dfs(parent, tree_off, prefix_len) -> perm, inv_perm, parent_new, plan
+    gather_rows(src, index)              -> src[index]
 """
-from ._binding import (MASK_WORDS, MAX_TREE, FwdCall, PlanResult, TreeAttnError, abi_version,
-                       build_tree, check_status, commit, fwd, library_path, load_library, num_splits, plan,
-                       prepare_fwd, workspace_bytes)
+from ._binding import (MASK_WORDS, MAX_TREE, FwdCall, PlanDfsResult, PlanResult, TreeAttnError,
+                       abi_version, build_tree, check_status, commit, fwd, gather_rows, library_path,
+                       load_library, num_splits, plan, plan_dfs, prepare_fwd, workspace_bytes)
 
-__all__ = ["MASK_WORDS", "MAX_TREE", "FwdCall", "PlanResult", "TreeAttnError", "abi_version",
-           "build_tree", "check_status", "commit", "fwd", "library_path", "load_library", "num_splits", "plan",
-           "prepare_fwd", "workspace_bytes"]
+__all__ = ["MASK_WORDS", "MAX_TREE", "FwdCall", "PlanDfsResult", "PlanResult", "TreeAttnError",
+           "abi_version", "build_tree", "check_status", "commit", "fwd", "gather_rows", "library_path",
+           "load_library", "num_splits", "plan", "plan_dfs", "prepare_fwd", "workspace_bytes"]

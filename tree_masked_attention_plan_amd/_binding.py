@@ -59,6 +59,10 @@ def load_library():
     lib.tree_attn_fwd_check.argtypes = fwd_args
     lib.tree_attn_build_tree.restype = ctypes.c_int
     lib.tree_attn_build_tree.argtypes = [P, i32, i32, i32, i32, P, P, P, P]
+    lib.tree_attn_plan_dfs.restype = ctypes.c_int
+    lib.tree_attn_plan_dfs.argtypes = [P, P, P, i32, i32, i32, P, P, P, P, P, P, P, P]
+    lib.tree_attn_gather_rows.restype = ctypes.c_int
+    lib.tree_attn_gather_rows.argtypes = [P, ctypes.c_int64, P, P, ctypes.c_int64, ctypes.c_int64, P]
     lib.tree_attn_commit.restype = ctypes.c_int
     lib.tree_attn_commit.argtypes = [P, P, P, P, P, P, P, P, P, P,
                                      i32, i32, i32, i32, i32, i32, i32, i32, ctypes.c_int, P, P, P]
@@ -138,6 +142,63 @@ def plan(parent: torch.Tensor, tree_off: torch.Tensor, prefix_len: torch.Tensor,
                                        int(max_tree), _ptr(out.anc_mask), _ptr(out.depth),
                                        _ptr(out.pos_id), _ptr(out.status), _stream(dev, stream))
     _raise(rc, "tree_attn_plan")
+    return out
+
+
+class PlanDfsResult(NamedTuple):
+    perm: torch.Tensor        # [N] int32: new global index -> old global index
+    inv_perm: torch.Tensor    # [N] int32: old -> new
+    parent_new: torch.Tensor  # [N] int32: local parents in the new labelling
+    plan: PlanResult          # the plan of the relabelled trees (rows in the new order)
+
+
+def plan_dfs(parent: torch.Tensor, tree_off: torch.Tensor, prefix_len: torch.Tensor,
+             max_tree: Optional[int] = None, *, stream=None) -> PlanDfsResult:
+    """The plan of every tree in a depth-first relabelling (preorder, roots
+    and children in increasing index), with the permutation that maps it to
+    the old labels.  Gather the rows of q / k_tree / v_tree with ``perm``
+    (:func:`gather_rows`) to run :func:`fwd` in the new order, and the rows
+    of its outputs with ``inv_perm`` to return to the old order."""
+    _dev_tensor(parent, "parent", torch.int32)
+    _dev_tensor(tree_off, "tree_off", torch.int32)
+    _dev_tensor(prefix_len, "prefix_len", torch.int32)
+    dev = parent.device
+    B = prefix_len.numel()
+    N = parent.numel()
+    if tree_off.numel() != B + 1:
+        raise ValueError("tree_off must have B+1 entries")
+    if max_tree is None:
+        max_tree = _max_tree_of(tree_off)
+    res = PlanDfsResult(torch.empty(N, dtype=torch.int32, device=dev),
+                        torch.empty(N, dtype=torch.int32, device=dev),
+                        torch.empty(N, dtype=torch.int32, device=dev),
+                        PlanResult(torch.empty((N, MASK_WORDS), dtype=torch.int64, device=dev),
+                                   torch.empty(N, dtype=torch.int32, device=dev),
+                                   torch.empty(N, dtype=torch.int32, device=dev),
+                                   torch.empty(B, dtype=torch.int32, device=dev)))
+    rc = load_library().tree_attn_plan_dfs(
+        _ptr(parent), _ptr(tree_off), _ptr(prefix_len), B, N, int(max_tree), _ptr(res.perm),
+        _ptr(res.inv_perm), _ptr(res.parent_new), _ptr(res.plan.anc_mask), _ptr(res.plan.depth),
+        _ptr(res.plan.pos_id), _ptr(res.plan.status), _stream(dev, stream))
+    _raise(rc, "tree_attn_plan_dfs")
+    return res
+
+
+def gather_rows(src: torch.Tensor, index: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """``out[i] = src[index[i]]`` along the first dimension (rows of any
+    contiguous device tensor; an index out of range gives a zero row)."""
+    _dev_tensor(index, "index", torch.int32)
+    if src.device != index.device or not src.is_contiguous():
+        raise ValueError("src must be a contiguous tensor on the index's device")
+    n_src = src.shape[0] if src.dim() > 0 else 0
+    row_bytes = src[0].numel() * src.element_size() if n_src > 0 else 0
+    if out is None:
+        out = torch.empty((index.numel(),) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    rc = load_library().tree_attn_gather_rows(_ptr(src), int(n_src), _ptr(index), _ptr(out),
+                                              int(index.numel()), int(row_bytes),
+                                              _stream(src.device, stream))
+    _raise(rc, "tree_attn_gather_rows")
     return out
 
 

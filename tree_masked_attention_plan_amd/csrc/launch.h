@@ -27,6 +27,29 @@ struct PlanParams {
     int32_t B, N, max_tree;
 };
 
+// depth-first relabelling: the plan's inputs and outputs (written in the new
+// labelling) plus the permutation, its inverse and the relabelled parents
+struct PlanDfsParams {
+    const int32_t *parent;
+    const int32_t *tree_off;
+    const int32_t *prefix_len;
+    int32_t *perm;          // [N] new global index -> old global index
+    int32_t *inv_perm;      // [N] old -> new
+    int32_t *parent_new;    // [N] local parents in the new labelling
+    uint64_t *anc_mask;
+    int32_t *depth;
+    int32_t *pos_id;
+    int32_t *status;
+    int32_t B, N, max_tree;
+};
+
+struct GatherParams {
+    const void *src;
+    const int32_t *index;
+    void *dst;
+    int64_t n_src, n_rows, row_bytes;
+};
+
 struct FwdParams {
     const void *q, *k_tree, *v_tree, *k_cache, *v_cache;
     const int32_t *block_table, *prefix_len, *tree_off;
@@ -68,6 +91,8 @@ constexpr int kTreeMaxPool = 16448;    // K * (T + 1) candidate slots
 constexpr int kTreeMaxLogp = 4096;     // Dmax * K
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t stream);
+hipError_t launch_plan_dfs(const PlanDfsParams &p, hipStream_t stream);
+hipError_t launch_gather(const GatherParams &p, hipStream_t stream);
 // best-first draft trees: one wave per request
 hipError_t launch_build_tree(const TreeParams &p, hipStream_t stream);
 // accepted-path commit: one workgroup per request

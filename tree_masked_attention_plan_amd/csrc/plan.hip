@@ -89,6 +89,136 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p_arg)
 }
 
 // ---------------------------------------------------------------------------
+// depth-first relabelling: one workgroup per request, one thread per node.
+// The order is the preorder of the forest with roots and children taken in
+// increasing local index.  In that order a node comes right after its parent
+// and the whole subtrees of its earlier siblings (for a root: the earlier
+// roots' subtrees), so with sz = subtree size and
+//   es[a] = sum of sz over the earlier siblings of a,
+// node v's new index is  sum over a on v's root path of es[a], plus the
+// number of v's proper ancestors.  Subtree sizes come from every node adding
+// one to each node on its root path (LDS atomics).
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void plan_dfs_kernel(PlanDfsParams p_arg)
+{
+    PlanDfsParams p = p_arg;
+    asm volatile("" : "+s"(p.parent), "+s"(p.tree_off), "+s"(p.prefix_len), "+s"(p.perm),
+                      "+s"(p.inv_perm), "+s"(p.parent_new), "+s"(p.anc_mask), "+s"(p.depth),
+                      "+s"(p.pos_id), "+s"(p.status), "+s"(p.B), "+s"(p.N), "+s"(p.max_tree));
+    __shared__ int32_t par[kMaxTree];
+    __shared__ int32_t rank[kMaxTree];
+    __shared__ int32_t sz[kMaxTree];
+    __shared__ int32_t es[kMaxTree];
+    __shared__ int32_t first_bad;
+    const int b = blockIdx.x;
+    const int j = threadIdx.x;
+    const int32_t L = gmem(p.prefix_len)[b];
+    const int32_t off = gmem(p.tree_off)[b];
+    const int32_t end = gmem(p.tree_off)[b + 1];
+    __builtin_amdgcn_sched_barrier(0);
+    const int32_t T = end - off;
+    // the plan's checks, in the plan's order (uniform early returns)
+    const bool bad_off = (T < 0) || (T > p.max_tree) || (off < 0) || (end > p.N) ||
+                         (b == 0 && off != 0) || (b == p.B - 1 && end != p.N);
+    if (bad_off || L < 0) {
+        if (j == 0)
+            gmem(p.status)[b] = bad_off ? kTreeBadOffsets : kTreeBadPrefix;
+        return;
+    }
+    if (j == 0)
+        first_bad = INT32_MAX;
+    int32_t pj = -1;
+    if (j < T) {
+        pj = gmem(p.parent)[off + j];
+        par[j] = pj;
+        sz[j] = 0;
+    }
+    __syncthreads();
+    if (j < T && (pj < -1 || pj >= j))
+        atomicMin(&first_bad, j);
+    __syncthreads();
+    const int32_t fb = first_bad;
+    if (fb != INT32_MAX) {
+        if (j == 0)
+            gmem(p.status)[b] = fb + 1;
+        return;
+    }
+    // subtree sizes: one for every node on each node's root path; the walk
+    // ends within j+1 steps since every parent precedes its child
+    int32_t d = 0;
+    if (j < T) {
+        for (int32_t a = j; a >= 0; a = par[a]) {
+            atomicAdd(&sz[a], 1);
+            ++d;
+        }
+    }
+    __syncthreads();
+    // earlier siblings' subtrees (all threads read the same s at once)
+    if (j < T) {
+        int32_t e = 0;
+        for (int32_t s = 0; s < j; ++s)
+            e += par[s] == pj ? sz[s] : 0;
+        es[j] = e;
+    }
+    __syncthreads();
+    if (j < T) {
+        int32_t r = d - 1;
+        for (int32_t a = j; a >= 0; a = par[a])
+            r += es[a];
+        // always in [0, T) for a valid tree; kept there regardless, so that
+        // no store below can leave the request's rows
+        rank[j] = min(max(r, 0), T - 1);
+    }
+    __syncthreads();
+    if (j < T) {
+        const int32_t r = rank[j];
+        gmem(p.perm)[off + r] = off + j;
+        gmem(p.inv_perm)[off + j] = off + r;
+        gmem(p.parent_new)[off + r] = pj < 0 ? -1 : rank[pj];
+        // the ancestor set in the new labels: bit rank[a] for every a in it
+        uint64_t n0 = 0, n1 = 0, n2 = 0, n3 = 0;
+        for (int32_t a = j; a >= 0; a = par[a]) {
+            const int32_t ra = rank[a];
+            const uint64_t bit = 1ull << (ra & 63);
+            const int word = ra >> 6;
+            n0 |= word == 0 ? bit : 0;
+            n1 |= word == 1 ? bit : 0;
+            n2 |= word == 2 ? bit : 0;
+            n3 |= word == 3 ? bit : 0;
+        }
+        __attribute__((address_space(1))) uint64_t *row = gmem(p.anc_mask) + (int64_t)(off + r) * kMaskWords;
+        row[0] = n0;
+        row[1] = n1;
+        row[2] = n2;
+        row[3] = n3;
+        gmem(p.depth)[off + r] = d;
+        gmem(p.pos_id)[off + r] = L + d - 1;
+    }
+    if (j == 0)
+        gmem(p.status)[b] = kTreeOk;
+}
+
+// ---------------------------------------------------------------------------
+// row gather: dst[i] = src[index[i]] for rows of row_bytes bytes (an index
+// outside [0, n_src) gives a zero row); V is the copy unit (16 or 4 bytes)
+// ---------------------------------------------------------------------------
+template <typename V>
+__global__ __launch_bounds__(256) void gather_rows_kernel(GatherParams p)
+{
+    const int64_t per_row = p.row_bytes / (int64_t)sizeof(V);
+    const V zero = {};
+    for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x) {
+        const int32_t i = p.index[row];
+        const bool ok = i >= 0 && i < p.n_src;
+        const V *s = (const V *)p.src + (ok ? (int64_t)i : 0) * per_row;
+        V *d = (V *)p.dst + row * per_row;
+        for (int64_t e = threadIdx.x; e < per_row; e += blockDim.x)
+            d[e] = ok ? s[e] : zero;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
 hipError_t launch_plan(const PlanParams &p, hipStream_t stream)
@@ -96,6 +226,29 @@ hipError_t launch_plan(const PlanParams &p, hipStream_t stream)
     if (p.B == 0)
         return hipSuccess;
     hipLaunchKernelGGL(plan_kernel, dim3(p.B), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan_dfs(const PlanDfsParams &p, hipStream_t stream)
+{
+    if (p.B == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(plan_dfs_kernel, dim3(p.B), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherParams &p, hipStream_t stream)
+{
+    if (p.n_rows == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)(p.n_rows < 65536 ? p.n_rows : 65536));
+    const bool v16 = p.row_bytes % 16 == 0 && ((uintptr_t)p.src | (uintptr_t)p.dst) % 16 == 0;
+    if (v16) {
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        hipLaunchKernelGGL((gather_rows_kernel<u32x4_t>), grid, dim3(256), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((gather_rows_kernel<uint32_t>), grid, dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

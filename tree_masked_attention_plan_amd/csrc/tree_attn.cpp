@@ -228,6 +228,59 @@ ta_status_t tree_attn_plan(const int32_t *parent, const int32_t *tree_off, const
     return ta::launch_plan(p, (hipStream_t)stream) == hipSuccess ? TA_OK : TA_ERR_HIP;
 }
 
+ta_status_t tree_attn_plan_dfs(const int32_t *parent, const int32_t *tree_off, const int32_t *prefix_len,
+                               int32_t B, int32_t N, int32_t max_tree, int32_t *perm, int32_t *inv_perm,
+                               int32_t *parent_new, uint64_t *anc_mask, int32_t *depth, int32_t *pos_id,
+                               int32_t *status, void *stream)
+{
+    if (max_tree > TREE_ATTN_MAX_TREE)
+        return TA_ERR_UNSUPPORTED;
+    if (B < 0 || N < 0 || max_tree < 0 || (int64_t)N > (int64_t)B * max_tree)
+        return TA_ERR_BAD_SHAPE;
+    if (B == 0)
+        return TA_OK;
+    if (!tree_off || !prefix_len || !status)
+        return TA_ERR_NULL_PTR;
+    if (N > 0 && (!parent || !perm || !inv_perm || !parent_new || !anc_mask || !depth || !pos_id))
+        return TA_ERR_NULL_PTR;
+    ta::PlanDfsParams p;
+    p.parent = parent;
+    p.tree_off = tree_off;
+    p.prefix_len = prefix_len;
+    p.perm = perm;
+    p.inv_perm = inv_perm;
+    p.parent_new = parent_new;
+    p.anc_mask = anc_mask;
+    p.depth = depth;
+    p.pos_id = pos_id;
+    p.status = status;
+    p.B = B;
+    p.N = N;
+    p.max_tree = max_tree;
+    return ta::launch_plan_dfs(p, (hipStream_t)stream) == hipSuccess ? TA_OK : TA_ERR_HIP;
+}
+
+ta_status_t tree_attn_gather_rows(const void *src, int64_t n_src, const int32_t *index, void *dst,
+                                  int64_t n_rows, int64_t row_bytes, void *stream)
+{
+    if (n_src < 0 || n_rows < 0 || row_bytes < 0 || row_bytes % 4 != 0 || n_src > INT32_MAX)
+        return TA_ERR_BAD_SHAPE;
+    if (n_rows == 0 || row_bytes == 0)
+        return TA_OK;
+    if (!index || !dst || (n_src > 0 && !src))
+        return TA_ERR_NULL_PTR;
+    if (((uintptr_t)src | (uintptr_t)dst) % 4 != 0)
+        return TA_ERR_UNSUPPORTED;
+    ta::GatherParams p;
+    p.src = src;
+    p.index = index;
+    p.dst = dst;
+    p.n_src = n_src;
+    p.n_rows = n_rows;
+    p.row_bytes = row_bytes;
+    return ta::launch_gather(p, (hipStream_t)stream) == hipSuccess ? TA_OK : TA_ERR_HIP;
+}
+
 ta_status_t tree_attn_build_tree(const float *logp, int32_t B, int32_t max_depth, int32_t K,
                                  int32_t T, int32_t *parent, int32_t *choice, float *score,
                                  void *stream)
