@@ -119,6 +119,10 @@ class Replica:
     def partial(self):
         self.call.partial()
 
+    def fwd(self):
+        self.call.partial()
+        self.call.merge()
+
 
 def replica_bytes(w: W.Workload) -> int:
     t = 0
@@ -152,6 +156,7 @@ class Runner:
         self.chunk = capture(lambda: [r.step() for r in reps], 1)
         self.single = [capture(r.step, 1) for r in reps]
         self.partial_chunk = capture(lambda: [r.partial() for r in reps], 1)
+        self.fwd_chunk = capture(lambda: [r.fwd() for r in reps], 1)
         torch.cuda.synchronize()
 
     def run_steps(self, k):
@@ -171,18 +176,20 @@ def time_steps(runner: Runner, steps: int, warmup: int) -> float:
     return time.perf_counter() - t0
 
 
-def time_partial_kernel(runner: Runner, min_launches: int = 200) -> float:
-    """Average duration (s) of one attention-kernel launch: HIP events on the
-    stream the graph's kernels run on, around back-to-back replays."""
+def time_partial_kernel(runner: Runner, min_launches: int = 200, graph=None) -> float:
+    """Average duration (s) of one attention-kernel launch (or, with
+    ``graph``, of one call of what it captured per replica): HIP events on
+    the stream the graph's kernels run on, around back-to-back replays."""
     R = len(runner.reps)
     reps = max(1, math.ceil(min_launches / R))
-    runner.partial_chunk.replay()
+    graph = runner.partial_chunk if graph is None else graph
+    graph.replay()
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
-        runner.partial_chunk.replay()
+        graph.replay()
     e1.record(stream)
     e1.synchronize()
     return e0.elapsed_time(e1) / 1e3 / (reps * R)
@@ -268,8 +275,9 @@ def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: flo
     dt = time_steps(runner, steps, warmup)
     ms = dt / steps * 1e3
     t_kern = time_partial_kernel(runner)
+    t_fwd = time_partial_kernel(runner, graph=runner.fwd_chunk)
     log(f"[bench] {name}: {ms * 1e3:.2f} us/step, attention kernel {t_kern * 1e6:.2f} us/launch, "
-        f"splits={nsplit}")
+        f"forward call (attention + merge) {t_fwd * 1e6:.2f} us, splits={nsplit}")
     res = {
         "workload": name,
         "value": wk["tree_tokens"] * steps / dt,
@@ -277,6 +285,9 @@ def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: flo
         "num_splits": nsplit,
         "tflops_step": wk["flops"] / (ms * 1e-3) / 1e12,
         "kernel_us": t_kern * 1e6,
+        # tree tokens per second of the forward call alone (attention kernel
+        # and split merge, the plan excluded), replayed back to back
+        "fwd_only": {"value": wk["tree_tokens"] / t_fwd, "unit": "tree tokens/s", "us": t_fwd * 1e6},
         "work": wk,
         "config": {"workload": name, "B": w.B, "tree_tokens": w.N, "max_tree": w.max_tree,
                    "prefix_tokens": int(w.prefix_len.sum()), "max_prefix": w.max_prefix,
@@ -544,13 +555,14 @@ def main():
     if "cpu_baseline" in main_res:
         line["cpu_baseline"] = main_res["cpu_baseline"]
     line["tflops"] = main_res["tflops_step"]
+    line["fwd_only"] = main_res["fwd_only"]
     if not args.no_secondary and args.workload != "moe":
         sec = measure("moe", max(20, args.steps // 10), max(2, args.warmup // 10), dev, cpu,
                       args.cpu_seconds)
         line["budget256"] = {"workload": "moe", "value": sec["value"], "unit": "tree tokens/s",
                              "ms_per_step": sec["ms_per_step"], "steps": max(20, args.steps // 10),
                              "tflops": sec["tflops_step"], "config": sec["config"],
-                             "roofline": sec["roofline"]}
+                             "roofline": sec["roofline"], "fwd_only": sec["fwd_only"]}
         if "cpu_baseline" in sec:
             line["budget256"]["cpu_baseline"] = sec["cpu_baseline"]
     if not args.no_secondary:
