@@ -191,6 +191,27 @@ def test_fwd_small_cases(dev, idx):
         assert_close(w, out, lse, o_ref, l_ref, f"{name} splits={ns}")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_large_and_jumping_scores(dev, dtype):
+    """Scores with a wide range whose running max jumps by far more than the
+    lazy-rescale slack from block to block: Q scaled by 4 and every physical
+    page's keys by its own factor in [0.1, 4] (the block table scatters
+    pages, so the magnitude jumps along each prefix and between splits)."""
+    rng = W.rng_for(21, 0)
+    w = small("rescale", [700, 129, 64], [W.best_first_tree(64, rng), W.chain(20), W.random_tree(30, 5, rng)],
+              D=64 if dtype == torch.float32 else 128, dtype=dtype, seed=21)
+    g = torch.Generator().manual_seed(21)
+    fac = (0.1 + 3.9 * torch.rand(w.k_cache.shape[0], generator=g)).view(-1, 1, 1, 1)
+    w.k_cache = (w.k_cache.float() * fac).to(dtype)    # sentinel NaN slots stay NaN
+    w.k_tree = (w.k_tree.float() * 2.5).to(dtype)
+    w.q = (w.q.float() * 4.0).to(dtype)
+    o_ref, l_ref = oracle.tree_attn_workload(w)
+    splits = (0, 1, 5, 64) if dtype == torch.bfloat16 else (0,)
+    for ns in splits:
+        out, lse = gpu_fwd(w, dev, num_splits=ns)
+        assert_close(w, out, lse, o_ref, l_ref, f"rescale {dtype} splits={ns}")
+
+
 def test_softmax_scale_override(dev):
     rng = W.rng_for(8, 0)
     w = small("scale", [90], [W.best_first_tree(30, rng)], seed=8)
