@@ -16,6 +16,11 @@
  *   tree_attn_plan  parent array  -> ancestor bitmask, depth, position ids
  *   tree_attn_fwd   GQA attention over the paged prefix plus the tree's own
  *                   K/V under the ancestor bitmask; online softmax; fp32 LSE
+ * and the steps next to it:
+ *   tree_attn_build_tree   best-first draft trees from per-depth candidates
+ *   tree_attn_commit       accepted root path -> the paged K/V cache
+ *   tree_attn_plan_dfs     the plan in a depth-first relabelling, plus the
+ *                          permutation (tree_attn_gather_rows moves rows)
  *
  * Conventions shared by every call:
  *  - All device buffers are allocated and owned by the caller; the library
