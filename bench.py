@@ -426,9 +426,10 @@ def measure_adjacent(dev) -> dict:
 
 
 def tree_blocks_visited(anc_mask: np.ndarray, tree_off: np.ndarray, G: int, rows_per_wg: int) -> int:
-    """(workgroup, 64-key tree block) pairs the attention kernel visits: a
-    workgroup's rows cover rows_per_wg / G consecutive nodes, and it copies
-    and computes a tree block when any of its nodes sees a key in it."""
+    """(row group, 64-key tree block) pairs with a visible key: a group of
+    rows_per_wg query rows covers rows_per_wg / G consecutive nodes, and a
+    workgroup holding those rows copies and computes a tree block when any
+    of its nodes sees a key in it."""
     words = anc_mask.view(np.uint64)
     total = 0
     per = max(1, rows_per_wg // G)
@@ -470,7 +471,7 @@ def measure_dfs(dev) -> dict:
         off = w.tree_off.cpu().numpy()
         G = w.Hq // w.Hkv
         geo = ta.num_splits(w.B, w.Hq, w.Hkv, w.D, mt, mp)
-        rows_wg = 256        # 8 row tiles of 32 query rows per workgroup at these shapes
+        rows_wg = 128        # counted per 128 query rows (4 row tiles of 32)
         vis_a = tree_blocks_visited(res.anc_mask.cpu().numpy(), off, G, rows_wg)
         vis_b = tree_blocks_visited(r.plan.anc_mask.cpu().numpy(), off, G, rows_wg)
         log(f"[bench] {name} attention: best-first labels {t_a * 1e6:.2f} us ({vis_a} tree blocks), "

@@ -173,6 +173,9 @@ def small_cases():
         ("fp32-d128", [45, 0], [W.best_first_tree(70, rng), W.chain(3)],
          dict(Hq=8, Hkv=2, D=128, dtype=torch.float32)),
         ("fp32-page4", [99], [W.best_first_tree(33, rng)], dict(D=64, dtype=torch.float32, ps=4)),
+        # enough (request, kv head, 128-row) units for the 4-wave workgroups
+        ("wide-batch", [int(x) for x in rng.integers(1, 400, 16)],
+         [W.best_first_tree(64, rng) for _ in range(16)], dict(Hq=32, Hkv=8)),
     ]
     return cases
 

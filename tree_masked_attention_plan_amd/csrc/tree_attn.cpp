@@ -15,6 +15,8 @@ namespace {
 // (8 / NW workgroups) per CU.  Splits are added until the grid fills that.
 constexpr int64_t kNumCUs = 256;
 constexpr int64_t kWavesPerCU = 8;
+// (request, kv head, 128-row tile) units from which 4-wave workgroups pay
+constexpr int64_t kWideUnits = 128;
 
 bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -85,6 +87,15 @@ Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tre
     const int32_t rows = max_tree * G;
     g.nr = waves_for(rows);
     g.ks = slices_for(g.nr, D);
+    // With plenty of work units, head_dim 128 runs 4-wave workgroups (4 row
+    // tiles, one slice) instead of 8-wave ones: two fit on a CU, and as
+    // independent workgroups (no shared barrier) one's softmax overlaps the
+    // other's MFMAs (measured: budget-256 and mixed batches 3-5 % faster; a
+    // single request, with few units, is not)
+    if (D == 128 && g.nr == 8 && (int64_t)B * Hkv * ceil_div(rows, 128) >= kWideUnits) {
+        g.nr = 4;
+        g.ks = 1;
+    }
     g.n_rt = rows > 0 ? (int32_t)ceil_div(rows, 32 * g.nr) : 1;
     const int32_t nw = g.nr * g.ks;
     // a step of the kernel covers this many prefix keys
