@@ -1052,7 +1052,7 @@ hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nr, int ks, hipStr
         else return hipErrorInvalidValue;
     } else {
         if (nr == 1 && ks == 4) launch_fwd_bf16_t<128, 1, 4>(p, stream);
-        else if (nr == 2 && ks == 4) launch_fwd_bf16_t<128, 2, 4>(p, stream);
+        else if (nr == 2 && ks == 2) launch_fwd_bf16_t<128, 2, 2>(p, stream);
         else if (nr == 4 && ks == 2) launch_fwd_bf16_t<128, 4, 2>(p, stream);
         else if (nr == 4 && ks == 1) launch_fwd_bf16_t<128, 4, 1>(p, stream);
         else if (nr == 8 && ks == 1) launch_fwd_bf16_t<128, 8, 1>(p, stream);

@@ -59,7 +59,10 @@ int32_t slices_for(int32_t nr, int32_t D)
 {
     if (nr >= 8)
         return 1;
-    if (D == 64 || nr == 4)
+    // two row tiles at head_dim 128 (budget 16): two slices, i.e. 4-wave
+    // workgroups, whose slice combine is half as long as with four
+    // (measured on the budget-16 layer: attention kernel 11.2 -> 10.0 us)
+    if (D == 64 || nr == 4 || (nr == 2 && D == 128))
         return 2;
     return 4;
 }
@@ -106,7 +109,10 @@ Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tre
             nslot = forced_splits;
         } else {
             const int64_t base = (int64_t)B * Hkv * g.n_rt;
-            const int64_t target = kNumCUs * (kWavesPerCU / nw);
+            // one workgroup per CU for the 4-wave budget-16 shape: more,
+            // smaller prefix chunks cost more in the merge than they gain
+            // (17 slots against 33 at chain16: 17.6 against 23.4 us a step)
+            const int64_t target = (g.nr == 2 && D == 128) ? kNumCUs : kNumCUs * (kWavesPerCU / nw);
             if (base > 0 && base < target)
                 nslot = ceil_div(target, base);
         }
