@@ -2,9 +2,11 @@
 """Throughput of tree-causal paged attention on one MI355X.
 
 One *step* is the whole hot path of one decode step over one batch of
-synthetic inputs: ``tree_attn_plan`` (parent array -> ancestor bitmask,
-depth, position ids) followed by ``tree_attn_fwd`` (its attention kernel and,
-when the prefix is split, the split-K merge).  Inputs are resident in HBM
+synthetic inputs: the plan (parent array -> ancestor bitmask, depth, position
+ids) and the attention (its kernel and, when the prefix is split, the split-K
+merge), run as one ``tree_attn_plan_fwd`` call, which builds the plan inside
+the attention kernel.  The same step as two calls (``tree_attn_plan``, then
+``tree_attn_fwd``) is reported beside it as ``two_call``.  Inputs are resident in HBM
 before timing starts; the step is replayed from HIP graphs so that the
 microsecond-scale launches are not limited by the Python launch rate, and
 successive steps rotate over enough input replicas that the working set does
@@ -108,16 +110,35 @@ class Replica:
                                    self.w.v_cache, self.w.block_table, self.w.prefix_len,
                                    self.w.tree_off, self.plan_out.anc_mask, max_tree=w.max_tree,
                                    max_prefix=w.max_prefix)
+        # the same step as one call: the plan built inside the attention
+        # kernel, into the same plan, output and workspace buffers
+        self.pcall = ta.prepare_plan_fwd(self.w.q, self.w.k_tree, self.w.v_tree, self.w.k_cache,
+                                         self.w.v_cache, self.w.block_table, self.w.prefix_len,
+                                         self.w.tree_off, self.w.parent, max_tree=w.max_tree,
+                                         max_prefix=w.max_prefix, plan_out=self.plan_out,
+                                         out=self.call.out, lse=self.call.lse,
+                                         workspace=self.call.workspace)
         self.max_tree = w.max_tree
+        # with fp32 the one call runs the plan kernel and the attention kernel
+        self.fused = w.dtype == torch.bfloat16
 
     def step(self):
+        """Plan + attention + merge: tree_attn_plan_fwd."""
+        self.pcall.run()
+
+    def step_two_call(self):
+        """The same step as tree_attn_plan, then tree_attn_fwd."""
         ta.plan(self.w.parent, self.w.tree_off, self.w.prefix_len, max_tree=self.max_tree,
                 out=self.plan_out)
         self.call.partial()
         self.call.merge()
 
     def partial(self):
-        self.call.partial()
+        """The attention kernel of the step alone."""
+        if self.fused:
+            self.pcall.partial()
+        else:
+            self.call.partial()
 
     def fwd(self):
         self.call.partial()
@@ -157,6 +178,7 @@ class Runner:
         self.single = [capture(r.step, 1) for r in reps]
         self.partial_chunk = capture(lambda: [r.partial() for r in reps], 1)
         self.fwd_chunk = capture(lambda: [r.fwd() for r in reps], 1)
+        self.two_call_chunk = capture(lambda: [r.step_two_call() for r in reps], 1)
         torch.cuda.synchronize()
 
     def run_steps(self, k):
@@ -276,8 +298,11 @@ def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: flo
     ms = dt / steps * 1e3
     t_kern = time_partial_kernel(runner)
     t_fwd = time_partial_kernel(runner, graph=runner.fwd_chunk)
-    log(f"[bench] {name}: {ms * 1e3:.2f} us/step, attention kernel {t_kern * 1e6:.2f} us/launch, "
-        f"forward call (attention + merge) {t_fwd * 1e6:.2f} us, splits={nsplit}")
+    t_two = time_partial_kernel(runner, graph=runner.two_call_chunk)
+    log(f"[bench] {name}: {ms * 1e3:.2f} us/step (one call: plan inside the attention kernel), "
+        f"attention kernel {t_kern * 1e6:.2f} us/launch; plan then forward as two calls "
+        f"{t_two * 1e6:.2f} us, forward call alone (attention + merge) {t_fwd * 1e6:.2f} us, "
+        f"splits={nsplit}")
     res = {
         "workload": name,
         "value": wk["tree_tokens"] * steps / dt,
@@ -288,6 +313,9 @@ def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: flo
         # tree tokens per second of the forward call alone (attention kernel
         # and split merge, the plan excluded), replayed back to back
         "fwd_only": {"value": wk["tree_tokens"] / t_fwd, "unit": "tree tokens/s", "us": t_fwd * 1e6},
+        # the same step as two calls (tree_attn_plan, then tree_attn_fwd),
+        # replayed back to back
+        "two_call": {"value": wk["tree_tokens"] / t_two, "unit": "tree tokens/s", "us": t_two * 1e6},
         "work": wk,
         "config": {"workload": name, "B": w.B, "tree_tokens": w.N, "max_tree": w.max_tree,
                    "prefix_tokens": int(w.prefix_len.sum()), "max_prefix": w.max_prefix,
@@ -557,13 +585,15 @@ def main():
         line["cpu_baseline"] = main_res["cpu_baseline"]
     line["tflops"] = main_res["tflops_step"]
     line["fwd_only"] = main_res["fwd_only"]
+    line["two_call"] = main_res["two_call"]
     if not args.no_secondary and args.workload != "moe":
         sec = measure("moe", max(20, args.steps // 10), max(2, args.warmup // 10), dev, cpu,
                       args.cpu_seconds)
         line["budget256"] = {"workload": "moe", "value": sec["value"], "unit": "tree tokens/s",
                              "ms_per_step": sec["ms_per_step"], "steps": max(20, args.steps // 10),
                              "tflops": sec["tflops_step"], "config": sec["config"],
-                             "roofline": sec["roofline"], "fwd_only": sec["fwd_only"]}
+                             "roofline": sec["roofline"], "fwd_only": sec["fwd_only"],
+                             "two_call": sec["two_call"]}
         if "cpu_baseline" in sec:
             line["budget256"]["cpu_baseline"] = sec["cpu_baseline"]
     if not args.no_secondary:

@@ -16,6 +16,8 @@
  *   tree_attn_plan  parent array  -> ancestor bitmask, depth, position ids
  *   tree_attn_fwd   GQA attention over the paged prefix plus the tree's own
  *                   K/V under the ancestor bitmask; online softmax; fp32 LSE
+ * (tree_attn_plan_fwd does both in one call, building the plan inside the
+ * attention kernel)
  * and the steps next to it:
  *   tree_attn_build_tree   best-first draft trees from per-depth candidates
  *   tree_attn_commit       accepted root path -> the paged K/V cache
@@ -180,6 +182,38 @@ ta_status_t tree_attn_fwd(const void *q, const void *k_tree, const void *v_tree,
                           size_t workspace_bytes, void *stream);
 
 /*
+ * tree_attn_plan_fwd -- tree_attn_plan and tree_attn_fwd in one call.
+ *
+ * The same tree-causal attention (JetFlow technical summary, section 2,
+ * tree-causal attention mask) computed from the parent array directly.  With
+ * bf16 the attention workgroups that own a request's tree stage its parents,
+ * check them and walk each node's root path themselves, so the plan costs
+ * no launch of its own and runs beside the prefix work; they also write the
+ * plan's outputs.  With fp32 (or N = 0) the call runs tree_attn_plan and
+ * then tree_attn_fwd on the stream.
+ *   q .. tree_off, B .. num_splits, out, lse, workspace: as tree_attn_fwd
+ *            (the same workspace size).
+ *   parent   [N] i32 (device): as tree_attn_plan.
+ *   anc_mask, depth, pos_id, status (device, written): exactly what
+ *            tree_attn_plan writes for these inputs, status codes included;
+ *            a later layer's tree_attn_fwd can take anc_mask as its input.
+ * Errors: the host checks of tree_attn_fwd, then the pointer rules of
+ *   tree_attn_plan.  For a request with a non-zero status, out and lse rows
+ *   are undefined (memory-safe), as after tree_attn_plan + tree_attn_fwd.
+ */
+ta_status_t tree_attn_plan_fwd(const void *q, const void *k_tree, const void *v_tree,
+                               const void *k_cache, const void *v_cache,
+                               const int32_t *block_table, const int32_t *prefix_len,
+                               const int32_t *tree_off, const int32_t *parent,
+                               int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                               int32_t page_size, int32_t num_pages,
+                               int32_t max_pages_per_seq, int32_t max_tree,
+                               int32_t max_prefix, float softmax_scale, ta_dtype_t dtype,
+                               int32_t num_splits, uint64_t *anc_mask, int32_t *depth,
+                               int32_t *pos_id, int32_t *status, void *out, float *lse,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * tree_attn_plan_dfs -- the plan, in a depth-first relabelling of each tree.
  *
  * The mask (JetFlow technical summary, section 2, tree-causal attention
@@ -333,6 +367,25 @@ ta_status_t tree_attn_merge(const void *q, const void *k_tree, const void *v_tre
                             int32_t max_prefix, float softmax_scale, ta_dtype_t dtype,
                             int32_t num_splits, void *out, float *lse, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/*
+ * The first stage of tree_attn_plan_fwd, with the same arguments and host
+ * checks: the plan and the attention kernel (for fp32 or N = 0, the plan
+ * kernel and tree_attn_fwd_partial).  tree_attn_plan_fwd is this followed by
+ * tree_attn_merge, called with the tree_attn_fwd arguments of the same call
+ * (anc_mask = the mask output).
+ */
+ta_status_t tree_attn_plan_fwd_partial(const void *q, const void *k_tree, const void *v_tree,
+                                       const void *k_cache, const void *v_cache,
+                                       const int32_t *block_table, const int32_t *prefix_len,
+                                       const int32_t *tree_off, const int32_t *parent,
+                                       int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                       int32_t page_size, int32_t num_pages,
+                                       int32_t max_pages_per_seq, int32_t max_tree,
+                                       int32_t max_prefix, float softmax_scale, ta_dtype_t dtype,
+                                       int32_t num_splits, uint64_t *anc_mask, int32_t *depth,
+                                       int32_t *pos_id, int32_t *status, void *out, float *lse,
+                                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The host-side argument check of tree_attn_fwd, on its own: returns exactly

@@ -38,6 +38,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("tree_attn_plan", "tree_attn_plan_dfs", "tree_attn_gather_rows", "tree_attn_fwd",
+                     "tree_attn_plan_fwd",
                      "tree_attn_workspace_bytes",
                      "tree_attn_num_splits", "tree_attn_fwd_check", "tree_attn_status_str",
                      "tree_attn_abi_version"):
@@ -138,8 +139,35 @@ def test_fwd_check_accepts_valid_arguments(lib):
 ])
 def test_fwd_check_rejects(lib, over, code):
     assert check(lib, **over) == code
-    # the full entry point returns the same code before any launch
+    # the full entry points return the same code before any launch
     assert call_fwd(lib, **over) == code
+    assert call_plan_fwd(lib, **over) == code
+
+
+def call_plan_fwd(lib, **over):
+    a = fwd_args(**over)
+    for k in ("parent", "depth", "pos_id", "status"):
+        a.setdefault(k, FAKE)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.tree_attn_plan_fwd(P(a["q"]), P(a["k_tree"]), P(a["v_tree"]), P(a["k_cache"]),
+                                  P(a["v_cache"]), P(a["block_table"]), P(a["prefix_len"]),
+                                  P(a["tree_off"]), P(a["parent"]), a["B"], a["N"], a["Hq"], a["Hkv"],
+                                  a["D"], a["page_size"], a["num_pages"], a["max_pages"], a["max_tree"],
+                                  a["max_prefix"], a["scale"], a["dtype"], a["num_splits"],
+                                  P(a["anc_mask"]), P(a["depth"]), P(a["pos_id"]), P(a["status"]),
+                                  P(a["out"]), P(a["lse"]), P(a["workspace"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over", [dict(parent=None), dict(depth=None), dict(pos_id=None),
+                                  dict(status=None), dict(status=None, dtype=FP32, D=64, Hq=4, Hkv=1)])
+def test_plan_fwd_pointer_rules(lib, over):
+    # the plan's pointers are checked after the forward's, before any launch
+    assert call_plan_fwd(lib, **over) == TA_ERR_NULL_PTR
+
+
+def test_plan_fwd_empty_batch_is_noop(lib):
+    assert call_plan_fwd(lib, B=0, N=0, q=None, out=None, lse=None, workspace=None, parent=None,
+                         anc_mask=None, depth=None, pos_id=None, status=None) == TA_OK
 
 
 def test_no_prefix_needs_no_cache_pointers(lib):

@@ -9,16 +9,20 @@ binding's entry points raises.
     plan(parent, tree_off, prefix_len)   -> anc_mask, depth, pos_id, status
     fwd(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
         tree_off, anc_mask)               -> out, lse
+    plan_fwd(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
+             tree_off, parent)            -> plan, out, lse  (one call)
     build_tree(logp, T)                 -> parent, choice, score
     commit(anc_mask, depth, tree_off, prefix_len, accepted, k_tree, v_tree,
            k_cache, v_cache, block_table)  -> new_prefix_len, status
     plan_dfs(parent, tree_off, prefix_len) -> perm, inv_perm, parent_new, plan
     gather_rows(src, index)              -> src[index]
 """
-from ._binding import (MASK_WORDS, MAX_TREE, FwdCall, PlanDfsResult, PlanResult, TreeAttnError,
-                       abi_version, build_tree, check_status, commit, fwd, gather_rows, library_path,
-                       load_library, num_splits, plan, plan_dfs, prepare_fwd, workspace_bytes)
+from ._binding import (MASK_WORDS, MAX_TREE, FwdCall, PlanDfsResult, PlanFwdCall, PlanResult,
+                       TreeAttnError, abi_version, build_tree, check_status, commit, fwd, gather_rows,
+                       library_path, load_library, num_splits, plan, plan_dfs, plan_fwd, prepare_fwd,
+                       prepare_plan_fwd, workspace_bytes)
 
-__all__ = ["MASK_WORDS", "MAX_TREE", "FwdCall", "PlanDfsResult", "PlanResult", "TreeAttnError",
-           "abi_version", "build_tree", "check_status", "commit", "fwd", "gather_rows", "library_path",
-           "load_library", "num_splits", "plan", "plan_dfs", "prepare_fwd", "workspace_bytes"]
+__all__ = ["MASK_WORDS", "MAX_TREE", "FwdCall", "PlanDfsResult", "PlanFwdCall", "PlanResult",
+           "TreeAttnError", "abi_version", "build_tree", "check_status", "commit", "fwd", "gather_rows",
+           "library_path", "load_library", "num_splits", "plan", "plan_dfs", "plan_fwd", "prepare_fwd",
+           "prepare_plan_fwd", "workspace_bytes"]

@@ -55,6 +55,9 @@ def load_library():
     for name in ("tree_attn_fwd", "tree_attn_fwd_partial", "tree_attn_merge"):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = fwd_args + [P]
+    for name in ("tree_attn_plan_fwd", "tree_attn_plan_fwd_partial"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = fwd_args[:9] + fwd_args[9:22] + [P, P, P, P] + fwd_args[22:] + [P]
     lib.tree_attn_fwd_check.restype = ctypes.c_int
     lib.tree_attn_fwd_check.argtypes = fwd_args
     lib.tree_attn_build_tree.restype = ctypes.c_int
@@ -417,3 +420,88 @@ def fwd(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, k_cache: to
                        num_splits=num_splits, out=out, lse=lse, workspace=workspace)
     call.run(stream)
     return call.out, call.lse
+
+
+class PlanFwdCall:
+    """One tree_attn_plan_fwd call with its arguments marshalled once.
+
+    ``run()`` enqueues the plan and the attention in one call on ``stream``
+    (default: the current stream at call time); ``partial()`` / ``merge()``
+    its two stages (tree_attn_plan_fwd_partial, then tree_attn_merge).
+    ``plan`` (a PlanResult), ``out`` and ``lse`` hold the results once the
+    stream reaches that point.
+    """
+
+    def __init__(self, args, fwd_args, plan_res, out, lse, workspace, nsplit):
+        self._args = args
+        self._fwd_args = fwd_args
+        self.plan = plan_res
+        self.out = out
+        self.lse = lse
+        self.workspace = workspace
+        self.num_splits = nsplit
+        self._lib = load_library()
+
+    def run(self, stream=None):
+        rc = self._lib.tree_attn_plan_fwd(*self._args, _stream(self.out.device, stream))
+        _raise(rc, "tree_attn_plan_fwd")
+        return self
+
+    def partial(self, stream=None):
+        rc = self._lib.tree_attn_plan_fwd_partial(*self._args, _stream(self.out.device, stream))
+        _raise(rc, "tree_attn_plan_fwd_partial")
+        return self
+
+    def merge(self, stream=None):
+        rc = self._lib.tree_attn_merge(*self._fwd_args, _stream(self.out.device, stream))
+        _raise(rc, "tree_attn_merge")
+        return self
+
+
+def prepare_plan_fwd(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, k_cache: torch.Tensor,
+                     v_cache: torch.Tensor, block_table: torch.Tensor, prefix_len: torch.Tensor,
+                     tree_off: torch.Tensor, parent: torch.Tensor, *, max_tree: Optional[int] = None,
+                     max_prefix: Optional[int] = None, scale: Optional[float] = None, num_splits: int = 0,
+                     plan_out: Optional[PlanResult] = None, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> PlanFwdCall:
+    """Check and marshal the arguments of a plan + forward call; see :func:`plan_fwd`."""
+    _dev_tensor(parent, "parent", torch.int32)
+    N, B = q.shape[0], prefix_len.numel()
+    if parent.numel() != N:
+        raise ValueError("parent must have N entries")
+    dev = q.device
+    if plan_out is None:
+        plan_out = PlanResult(torch.empty((N, MASK_WORDS), dtype=torch.int64, device=dev),
+                              torch.empty(N, dtype=torch.int32, device=dev),
+                              torch.empty(N, dtype=torch.int32, device=dev),
+                              torch.empty(B, dtype=torch.int32, device=dev))
+    else:
+        _dev_tensor(plan_out.depth, "depth", torch.int32)
+        _dev_tensor(plan_out.pos_id, "pos_id", torch.int32)
+        _dev_tensor(plan_out.status, "status", torch.int32)
+        if plan_out.depth.numel() != N or plan_out.pos_id.numel() != N or plan_out.status.numel() != B:
+            raise ValueError("plan_out must hold [N] depth / pos_id and [B] status")
+    # the forward's own checks and marshalling, with the plan's mask output in
+    # place of the mask input
+    call = prepare_fwd(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, tree_off,
+                       plan_out.anc_mask, max_tree=max_tree, max_prefix=max_prefix, scale=scale,
+                       num_splits=num_splits, out=out, lse=lse, workspace=workspace)
+    a = call._args
+    args = (a[:8] + (_ptr(parent),) + a[9:22] +
+            (_ptr(plan_out.anc_mask), _ptr(plan_out.depth), _ptr(plan_out.pos_id), _ptr(plan_out.status)) +
+            a[22:])
+    return PlanFwdCall(args, a, plan_out, call.out, call.lse, call.workspace, call.num_splits)
+
+
+def plan_fwd(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, k_cache: torch.Tensor,
+             v_cache: torch.Tensor, block_table: torch.Tensor, prefix_len: torch.Tensor,
+             tree_off: torch.Tensor, parent: torch.Tensor, *, max_tree: Optional[int] = None,
+             max_prefix: Optional[int] = None, scale: Optional[float] = None, num_splits: int = 0,
+             stream=None) -> Tuple[PlanResult, torch.Tensor, torch.Tensor]:
+    """:func:`plan` and :func:`fwd` in one call (tree_attn_plan_fwd): returns
+    ``(plan, out, lse)``, the plan exactly as :func:`plan` writes it."""
+    call = prepare_plan_fwd(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, tree_off, parent,
+                            max_tree=max_tree, max_prefix=max_prefix, scale=scale, num_splits=num_splits)
+    call.run(stream)
+    return call.plan, call.out, call.lse

@@ -275,6 +275,11 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     char *const v_st1 = kv_lds + 3 * SBYTES;
     // running (max, sum) of every slice's rows, for the final combine
     __shared__ float2 ml_x[KS > 1 ? NR * KS * 32 : 1];
+    // the request's parents and first bad node, when the plan is built here
+    __shared__ int32_t par_l[kMaxTree];
+    __shared__ int32_t first_bad_l;
+    // one word per wave for each of the two workgroup-wide ORs below
+    __shared__ uint32_t red_l[2][NW];
 
     Unit u;
     if (!decode_unit(p, u))
@@ -304,10 +309,29 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
         for (int q = 0; q < 4 * KSB; ++q)
             asm volatile("" : "+s"(pg0[q]));
     }
+    // With a parent array the units that own a request's tree also build its
+    // plan.  The request-level checks come first, on the raw geometry, with
+    // the plan's status codes.
+    const bool fuse = p.parent != nullptr;
+    int req_status = kTreeOk;
+    int L_raw = 0;
+    if (fuse && R.owns_tree) {
+        const int off_raw = ((cint_p)p.tree_off)[u.b];
+        const int end_raw = ((cint_p)p.tree_off)[u.b + 1];
+        L_raw = ((cint_p)p.prefix_len)[u.b];
+        const int T_raw = end_raw - off_raw;
+        const bool bad_off = T_raw < 0 || T_raw > p.max_tree || off_raw < 0 || end_raw > p.N ||
+                             (u.b == 0 && off_raw != 0) || (u.b == p.B - 1 && end_raw != p.N);
+        req_status = bad_off ? kTreeBadOffsets : (L_raw < 0 ? kTreeBadPrefix : kTreeOk);
+    }
     const int rows = R.T * p.G;
     const int row0 = u.rt * (NR * 32);
-    if (row0 >= rows)
+    if (row0 >= rows) {
+        // an empty tree (or one whose clamped size is 0) still gets a status
+        if (fuse && R.owns_tree && u.c == 0 && u.rt == 0 && threadIdx.x == 0)
+            gmem(p.plan_status)[u.b] = req_status;
         return;   // uniform across the workgroup
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -487,6 +511,15 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
         // fall back to the block's first key, so only valid pages are used
         issue_dma(0, StageTag<0>(), StageTag<1>());
     }
+    // A tree-only unit of a request whose tree fits one 64-node block needs
+    // that block whatever the mask words say (every row sees its own node),
+    // so its copy starts here too, before the mask words (or the parents)
+    // are read.
+    const bool early_tree = R.owns_tree && n_pre == 0 && R.T <= 64;
+    if (early_tree) {
+        tree_need = 1;
+        issue_dma(0, StageTag<0>(), StageTag<0>());
+    }
 
     // Q^T fragments (B operand): lane holds Q[row][kc*16 + hh*8 .. +8]
     bf16x8 qf[NKC];
@@ -502,18 +535,112 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     }
 
     // tree blocks this workgroup needs (only the unit that owns the tree)
+    // OR of four per-lane flag bits over the workgroup: a ballot per bit in
+    // each wave, one LDS word per wave, one barrier (slot: which of the two
+    // uses, each made once)
+    auto block_or4 = [&](uint32_t bits, int slot) __attribute__((always_inline)) -> uint32_t {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            v |= (__ballot((bits >> b) & 1u) != 0ull) ? (1u << b) : 0u;
+        if (lane == 0)
+            red_l[slot][wv] = v;
+        __syncthreads();
+        uint32_t r = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            r |= red_l[slot][w];
+        return r;
+    };
+
     uint64_t mw[kMaskWords] = {0, 0, 0, 0};
     if (R.owns_tree) {
-        if (row_ok) {
+        if (fuse) {
+            // Stage the request's parents and check them as the plan does
+            // (parent[j] in [-1, j)); then each row walks its node's parent
+            // chain, which ends within node + 1 steps.  Units of kv head 0
+            // write the plan's outputs: one row per node (its group's first
+            // q head) and, from row tile 0, the request's status.
+            constexpr int NPT = (kMaxTree + NW * 64 - 1) / (NW * 64);   // parents per thread
+            uint32_t badp = 0;
+            if (req_status == kTreeOk) {
+                const auto pg = gmem(p.parent) + R.off;
+                int pj[NPT];
+#pragma unroll
+                for (int i = 0; i < NPT; ++i) {
+                    const int j = tid + i * NW * 64;
+                    pj[i] = j < R.T ? pg[j] : -1;
+                }
+#pragma unroll
+                for (int i = 0; i < NPT; ++i) {
+                    const int j = tid + i * NW * 64;
+                    if (j < R.T) {
+                        par_l[j] = pj[i];
+                        badp |= (pj[i] < -1 || pj[i] >= j) ? 1u : 0u;
+                    }
+                }
+            }
+            if (block_or4(badp, 0)) {
+                if (tid == 0)
+                    first_bad_l = INT32_MAX;
+                __syncthreads();
+                for (int j = tid; j < R.T; j += NW * 64) {
+                    const int pj = par_l[j];
+                    if (pj < -1 || pj >= j)
+                        atomicMin(&first_bad_l, j);
+                }
+                __syncthreads();
+                req_status = first_bad_l + 1;
+            }
+            if (req_status == kTreeOk && row_ok) {
+                uint64_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+                int d = 0;
+                if (R.T <= 64) {
+                    // one mask word: the shortest loop (the walk's steps are
+                    // dependent LDS reads)
+                    for (int a = node; a >= 0; a = par_l[a]) {
+                        w0 |= 1ull << a;
+                        ++d;
+                    }
+                } else {
+                    for (int a = node; a >= 0; a = par_l[a]) {
+                        const uint64_t bit = 1ull << (a & 63);
+                        const int word = a >> 6;
+                        w0 |= word == 0 ? bit : 0ull;
+                        w1 |= word == 1 ? bit : 0ull;
+                        w2 |= word == 2 ? bit : 0ull;
+                        w3 |= word == 3 ? bit : 0ull;
+                        ++d;
+                    }
+                }
+                mw[0] = w0;
+                mw[1] = w1;
+                mw[2] = w2;
+                mw[3] = w3;
+                if (c == 0 && hh == 0 && ks == 0 && my_row == node * p.G) {
+                    const int64_t n = R.off + node;
+                    const auto mrow = gmem(p.plan_mask) + n * kMaskWords;
+                    mrow[0] = w0;
+                    mrow[1] = w1;
+                    mrow[2] = w2;
+                    mrow[3] = w3;
+                    gmem(p.plan_depth)[n] = d;
+                    gmem(p.plan_pos)[n] = L_raw + d - 1;
+                }
+            }
+            if (c == 0 && u.rt == 0 && tid == 0)
+                gmem(p.plan_status)[u.b] = req_status;
+        } else if (row_ok) {
             const auto mrow = gmem(p.anc_mask + (int64_t)(R.off + node) * kMaskWords);
 #pragma unroll
             for (int w = 0; w < kMaskWords; ++w)
                 mw[w] = (w * 64 < R.T) ? mrow[w] : 0ull;
         }
+        uint32_t nz = 0;
 #pragma unroll
         for (int w = 0; w < kMaskWords; ++w)
-            if (__syncthreads_or(mw[w] != 0ull))
-                tree_need |= 1 << w;
+            nz |= mw[w] != 0ull ? (1u << w) : 0u;
+        tree_need |= (int)block_or4(nz, 1);
     }
     const int n_blocks = n_pre + __builtin_popcount(tree_need);
     const int n_steps = (n_blocks + KSB - 1) / KSB;
@@ -695,7 +822,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     // which does not see the DMA, then has no load of its own outstanding
     // inside the loop and inserts no waits there.
     TA_WAIT_VMCNT(0);
-    if (!early && n_steps > 0)
+    if (!early && !early_tree && n_steps > 0)
         issue_dma(0, StageTag<0>(), StageTag<0>());
     for (int j = 0; j < n_steps; j += 2) {
         step(j, StageTag<0>());

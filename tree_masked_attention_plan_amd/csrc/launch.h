@@ -64,6 +64,13 @@ struct FwdParams {
     int32_t n_rt;                   // row tiles per (request, kv head)
     int32_t units, units_per_xcd;   // work units and their per-XCD share
     float c2;                       // softmax scale * log2(e)
+    // Plan built inside the attention kernel (bf16 only): with parent set,
+    // the workgroups that own a request's tree derive the ancestor masks from
+    // the parent array instead of reading anc_mask, and write the plan's
+    // outputs (all four are then set; null otherwise).
+    const int32_t *parent;
+    uint64_t *plan_mask;
+    int32_t *plan_depth, *plan_pos, *plan_status;
 };
 
 struct CommitParams {

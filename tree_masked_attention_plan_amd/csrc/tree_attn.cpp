@@ -424,13 +424,21 @@ namespace {
 
 enum Stage { kStagePartial = 1, kStageMerge = 2, kStageBoth = 3 };
 
+// the plan's inputs and outputs when the attention kernel builds the plan
+struct FusedPlan {
+    const int32_t *parent;
+    uint64_t *anc_mask;
+    int32_t *depth, *pos_id, *status;
+};
+
 ta_status_t run_fwd(const void *q, const void *k_tree, const void *v_tree, const void *k_cache,
                     const void *v_cache, const int32_t *block_table, const int32_t *prefix_len,
                     const int32_t *tree_off, const uint64_t *anc_mask, int32_t B, int32_t N,
                     int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
                     int32_t max_pages_per_seq, int32_t max_tree, int32_t max_prefix,
                     float softmax_scale, ta_dtype_t dtype, int32_t num_splits, void *out, float *lse,
-                    void *workspace, size_t workspace_bytes, void *stream, int stages)
+                    void *workspace, size_t workspace_bytes, void *stream, int stages,
+                    const FusedPlan *fp = nullptr)
 {
     const ta_status_t st = check_fwd(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
                                      tree_off, anc_mask, B, N, Hq, Hkv, D, page_size, num_pages,
@@ -478,6 +486,11 @@ ta_status_t run_fwd(const void *q, const void *k_tree, const void *v_tree, const
     p.units_per_xcd = (int32_t)ceil_div(units, 8);
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
     p.c2 = scale * 1.44269504088896340736f;
+    p.parent = fp ? fp->parent : nullptr;
+    p.plan_mask = fp ? fp->anc_mask : nullptr;
+    p.plan_depth = fp ? fp->depth : nullptr;
+    p.plan_pos = fp ? fp->pos_id : nullptr;
+    p.plan_status = fp ? fp->status : nullptr;
     hipStream_t s = (hipStream_t)stream;
     if (stages & kStagePartial) {
         if (ta::launch_fwd(p, dtype == TA_DTYPE_FP32, g.nr, g.ks, s) != hipSuccess)
@@ -511,5 +524,70 @@ ta_status_t tree_attn_fwd(TA_FWD_PARAMS) { return run_fwd(TA_FWD_ARGS, kStageBot
 ta_status_t tree_attn_fwd_partial(TA_FWD_PARAMS) { return run_fwd(TA_FWD_ARGS, kStagePartial); }
 
 ta_status_t tree_attn_merge(TA_FWD_PARAMS) { return run_fwd(TA_FWD_ARGS, kStageMerge); }
+
+}  // extern "C"
+
+namespace {
+
+ta_status_t run_plan_fwd(const void *q, const void *k_tree, const void *v_tree, const void *k_cache,
+                         const void *v_cache, const int32_t *block_table, const int32_t *prefix_len,
+                         const int32_t *tree_off, const int32_t *parent, int32_t B, int32_t N, int32_t Hq,
+                         int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                         int32_t max_pages_per_seq, int32_t max_tree, int32_t max_prefix,
+                         float softmax_scale, ta_dtype_t dtype, int32_t num_splits, uint64_t *anc_mask,
+                         int32_t *depth, int32_t *pos_id, int32_t *status, void *out, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream, int stages)
+{
+    const ta_status_t st = check_fwd(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
+                                     tree_off, anc_mask, B, N, Hq, Hkv, D, page_size, num_pages,
+                                     max_pages_per_seq, max_tree, max_prefix, softmax_scale, dtype,
+                                     num_splits, out, lse, workspace, workspace_bytes);
+    if (st != TA_OK || B == 0)
+        return st;
+    // the plan's own pointer rules
+    if (!tree_off || !prefix_len || !status)
+        return TA_ERR_NULL_PTR;
+    if (N > 0 && (!parent || !anc_mask || !depth || !pos_id))
+        return TA_ERR_NULL_PTR;
+    if (dtype == TA_DTYPE_FP32 || N == 0) {
+        // the fp32 kernel reads the mask words: plan first, then attention
+        const ta_status_t sp = tree_attn_plan(parent, tree_off, prefix_len, B, N, max_tree, anc_mask, depth,
+                                              pos_id, status, stream);
+        if (sp != TA_OK)
+            return sp;
+        return run_fwd(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, tree_off, anc_mask, B,
+                       N, Hq, Hkv, D, page_size, num_pages, max_pages_per_seq, max_tree, max_prefix,
+                       softmax_scale, dtype, num_splits, out, lse, workspace, workspace_bytes, stream,
+                       stages);
+    }
+    const FusedPlan fp = {parent, anc_mask, depth, pos_id, status};
+    return run_fwd(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, tree_off, anc_mask, B, N,
+                   Hq, Hkv, D, page_size, num_pages, max_pages_per_seq, max_tree, max_prefix, softmax_scale,
+                   dtype, num_splits, out, lse, workspace, workspace_bytes, stream, stages, &fp);
+}
+
+}  // namespace
+
+#define TA_PLAN_FWD_PARAMS                                                                               \
+    const void *q, const void *k_tree, const void *v_tree, const void *k_cache, const void *v_cache,     \
+        const int32_t *block_table, const int32_t *prefix_len, const int32_t *tree_off,                  \
+        const int32_t *parent, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,                 \
+        int32_t page_size, int32_t num_pages, int32_t max_pages_per_seq, int32_t max_tree,               \
+        int32_t max_prefix, float softmax_scale, ta_dtype_t dtype, int32_t num_splits,                   \
+        uint64_t *anc_mask, int32_t *depth, int32_t *pos_id, int32_t *status, void *out, float *lse,     \
+        void *workspace, size_t workspace_bytes, void *stream
+#define TA_PLAN_FWD_ARGS                                                                                 \
+    q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, tree_off, parent, B, N, Hq, Hkv, D,    \
+        page_size, num_pages, max_pages_per_seq, max_tree, max_prefix, softmax_scale, dtype, num_splits, \
+        anc_mask, depth, pos_id, status, out, lse, workspace, workspace_bytes, stream
+
+extern "C" {
+
+ta_status_t tree_attn_plan_fwd(TA_PLAN_FWD_PARAMS) { return run_plan_fwd(TA_PLAN_FWD_ARGS, kStageBoth); }
+
+ta_status_t tree_attn_plan_fwd_partial(TA_PLAN_FWD_PARAMS)
+{
+    return run_plan_fwd(TA_PLAN_FWD_ARGS, kStagePartial);
+}
 
 }  // extern "C"
