@@ -66,14 +66,16 @@ def node_depths(w: W.Workload) -> np.ndarray:
 
 
 def work(w: W.Workload, nsplit: int) -> dict:
-    """Algorithmic work of one forward call, over visible (query, key) pairs.
+    """Algorithmic work of one step (plan and attention in one call), over
+    visible (query, key) pairs.
 
     flops = 4 * D * Hq * (sum_b T_b * L_b + sum_i depth_i)   (QK^T and PV)
-    bytes = valid prefix K/V + tree K/V + Q + O + LSE + mask words that can
-            hold a visible bit (ceil(T_b / 64) per node) + live block-table
-            entries.  ``kernel_bytes`` is the part the attention kernel itself
-            must move: everything but O and LSE when a separate merge writes
-            them (split count > 1)."""
+    bytes = valid prefix K/V + tree K/V + Q + O + LSE + the parent array read
+            and the plan's outputs written (mask words that can hold a
+            visible bit, ceil(T_b / 64) per node, depth, position id, status)
+            + live block-table entries.  ``kernel_bytes`` is the part the
+            attention kernel itself must move: everything but O and LSE when
+            a separate merge writes them (split count > 1)."""
     e = torch.tensor([], dtype=w.dtype).element_size()
     T = w.tree_sizes
     L = w.prefix_len.numpy().astype(np.int64)
@@ -84,9 +86,9 @@ def work(w: W.Workload, nsplit: int) -> dict:
     kv = int(L.sum()) * w.Hkv * w.D * 2 * e + N * w.Hkv * w.D * 2 * e
     q = N * w.Hq * w.D * e
     o = N * w.Hq * w.D * e + N * w.Hq * 4
-    mask = int((T * ((T + 63) // 64)).sum()) * 8
+    plan = N * 4 + int((T * ((T + 63) // 64)).sum()) * 8 + N * 8 + w.B * 4
     bt = int(((L + w.page_size - 1) // w.page_size).sum()) * 4
-    total = kv + q + o + mask + bt
+    total = kv + q + o + plan + bt
     kernel = total if nsplit == 1 else total - o
     return {"flops": flops, "bytes": float(total), "kernel_bytes": float(kernel),
             "pairs": pairs, "sum_depth": sdepth, "tree_tokens": N}
@@ -165,7 +167,7 @@ class Runner:
     turn, ``single[r]`` one step on replica r, ``partial_chunk`` only the
     attention kernel on every replica (for the per-launch kernel time)."""
 
-    def __init__(self, reps):
+    def __init__(self, reps, compare=True):
         self.reps = reps
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -177,8 +179,11 @@ class Runner:
         self.chunk = capture(lambda: [r.step() for r in reps], 1)
         self.single = [capture(r.step, 1) for r in reps]
         self.partial_chunk = capture(lambda: [r.partial() for r in reps], 1)
-        self.fwd_chunk = capture(lambda: [r.fwd() for r in reps], 1)
-        self.two_call_chunk = capture(lambda: [r.step_two_call() for r in reps], 1)
+        # the comparison forms launch the same attention kernel symbol; a
+        # profiling run can leave them out so that its trace holds the step's
+        # launches only
+        self.fwd_chunk = capture(lambda: [r.fwd() for r in reps], 1) if compare else None
+        self.two_call_chunk = capture(lambda: [r.step_two_call() for r in reps], 1) if compare else None
         torch.cuda.synchronize()
 
     def run_steps(self, k):
@@ -283,7 +288,8 @@ def traffic_for(workload: str):
 
 # ---------------------------------------------------------------- main
 
-def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: float) -> dict:
+def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: float,
+            compare: bool = True) -> dict:
     w = W.make_config(name)
     per = replica_bytes(w)
     R = max(1, min(MAX_REPLICAS, math.ceil(ROTATE_BYTES / per)))
@@ -291,14 +297,14 @@ def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: flo
         f"replicas={R} ({per / 2**20:.1f} MiB each)")
     reps = [Replica(w, dev) for _ in range(R)]
     ta.check_status(reps[0].plan_out.status)
-    runner = Runner(reps)
+    runner = Runner(reps, compare)
     nsplit = reps[0].call.num_splits
     wk = work(w, nsplit)
     dt = time_steps(runner, steps, warmup)
     ms = dt / steps * 1e3
     t_kern = time_partial_kernel(runner)
-    t_fwd = time_partial_kernel(runner, graph=runner.fwd_chunk)
-    t_two = time_partial_kernel(runner, graph=runner.two_call_chunk)
+    t_fwd = time_partial_kernel(runner, graph=runner.fwd_chunk) if compare else float("nan")
+    t_two = time_partial_kernel(runner, graph=runner.two_call_chunk) if compare else float("nan")
     log(f"[bench] {name}: {ms * 1e3:.2f} us/step (one call: plan inside the attention kernel), "
         f"attention kernel {t_kern * 1e6:.2f} us/launch; plan then forward as two calls "
         f"{t_two * 1e6:.2f} us, forward call alone (attention + merge) {t_fwd * 1e6:.2f} us, "
@@ -312,10 +318,12 @@ def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: flo
         "kernel_us": t_kern * 1e6,
         # tree tokens per second of the forward call alone (attention kernel
         # and split merge, the plan excluded), replayed back to back
-        "fwd_only": {"value": wk["tree_tokens"] / t_fwd, "unit": "tree tokens/s", "us": t_fwd * 1e6},
+        "fwd_only": ({"value": wk["tree_tokens"] / t_fwd, "unit": "tree tokens/s", "us": t_fwd * 1e6}
+                     if compare else None),
         # the same step as two calls (tree_attn_plan, then tree_attn_fwd),
         # replayed back to back
-        "two_call": {"value": wk["tree_tokens"] / t_two, "unit": "tree tokens/s", "us": t_two * 1e6},
+        "two_call": ({"value": wk["tree_tokens"] / t_two, "unit": "tree tokens/s", "us": t_two * 1e6}
+                     if compare else None),
         "work": wk,
         "config": {"workload": name, "B": w.B, "tree_tokens": w.N, "max_tree": w.max_tree,
                    "prefix_tokens": int(w.prefix_len.sum()), "max_prefix": w.max_prefix,
@@ -534,6 +542,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the budget-256 (moe) measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the two-call and forward-only timings (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain copy kernel of this many MiB (counter calibration)")
@@ -563,7 +573,8 @@ def main():
     ta.load_library()
     dev = torch.device("cuda:0")
     cpu = not args.no_cpu_baseline
-    main_res = measure(args.workload, args.steps, args.warmup, dev, cpu, args.cpu_seconds)
+    main_res = measure(args.workload, args.steps, args.warmup, dev, cpu, args.cpu_seconds,
+                       not args.no_compare)
     w_dtype = "f32" if args.workload == "tiny" else "bf16"
     line = {
         "metric": METRIC,
@@ -588,7 +599,7 @@ def main():
     line["two_call"] = main_res["two_call"]
     if not args.no_secondary and args.workload != "moe":
         sec = measure("moe", max(20, args.steps // 10), max(2, args.warmup // 10), dev, cpu,
-                      args.cpu_seconds)
+                      args.cpu_seconds, not args.no_compare)
         line["budget256"] = {"workload": "moe", "value": sec["value"], "unit": "tree tokens/s",
                              "ms_per_step": sec["ms_per_step"], "steps": max(20, args.steps // 10),
                              "tflops": sec["tflops_step"], "config": sec["config"],
