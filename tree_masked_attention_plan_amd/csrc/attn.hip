@@ -399,6 +399,42 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
         vofs[i] = rb + LY::swz_v(dma_row[i], dma_pos) * 16;
     }
 
+    // Full prefix blocks (SP): the wave's rows [wrow0, wrow0 + NIW * RPI)
+    // fall in GPW groups of 16 rows, each inside one page.  The page id of
+    // every group is read one step ahead (pf_pg, scalar loads that complete
+    // during the step in between), and each group's rows are addressed from
+    // one uniform base: the row inside the group moves into the lane's
+    // constant offset.
+    constexpr int WROWS = NIW * LY::RPI;                  // rows per wave per step
+    constexpr int GPW = WROWS >= 16 ? WROWS / 16 : 1;     // 16-row groups per wave
+    const int wrow0 = ((wv * NIW) % LY::NINST) * LY::RPI; // the wave's first row in its block
+    const int grp0 = wrow0 & ~15;                         // first row of its first group
+    uint32_t kofs_g[NIW], vofs_g[NIW];
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) {
+        const uint32_t in_grp = (uint32_t)((wrow0 + i * LY::RPI - grp0) & 15) * (uint32_t)row_bytes;
+        kofs_g[i] = kofs[i] + in_grp;
+        vofs_g[i] = vofs[i] + in_grp;
+    }
+    int pf_pg[GPW];
+#pragma unroll
+    for (int g = 0; g < GPW; ++g)
+        pf_pg[g] = 0;
+    // page ids of step j's groups, for a later non-first issue of step j
+    auto prefetch_pages = [&](int j) __attribute__((always_inline)) {
+        if (!SP)
+            return;
+        const int k = j * KSB + dma_blk;
+        if (k >= n_pre)
+            return;
+        const int t0 = R.kstart + k * 64 + grp0;
+#pragma unroll
+        for (int g = 0; g < GPW; ++g) {
+            const int t = t0 + g * 16;
+            pf_pg[g] = t < R.kend ? btc[t >> p.page_shift] : 0;
+        }
+    };
+
     // Issue this wave's copies of step j into a stage.  Page ids are fetched
     // so that no vector load sits between two steps' DMA batches (the vmcnt
     // waits below count DMA instructions only): with SP they come from scalar
@@ -416,6 +452,27 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
         char *vst = (decltype(stage)::value == 0 ? v_st0 : v_st1) + dma_blk * LY::BLK;
         const uint16_t *kb = (const uint16_t *)(is_tree ? kt_p : kc_p);
         const uint16_t *vb = (const uint16_t *)(is_tree ? vt_p : vc_p);
+        if (SP && !is_tree && !FIRST && start + 64 <= R.kend) {
+            // a full prefix block whose group page ids were prefetched
+#pragma unroll
+            for (int g = 0; g < GPW; ++g) {
+                int page = pf_pg[g];
+                page = page < 0 ? 0 : (page >= p.num_pages ? p.num_pages - 1 : page);
+                const int tg = start + grp0 + g * 16;   // the group's first key
+                const int64_t gb = (((int64_t)page << p.page_shift) + (tg & pmask)) * row_bytes;
+#pragma unroll
+                for (int i = 0; i < NIW; ++i) {
+                    if (((wrow0 + i * LY::RPI - grp0) >> 4) != g)
+                        continue;   // compile-time for a given wave shape
+                    const int gl = (wv * NIW + i) % LY::NINST;
+                    const uint32_t ldsk = __builtin_amdgcn_readfirstlane(lds_addr(kst) + gl * 1024);
+                    const uint32_t ldsv = __builtin_amdgcn_readfirstlane(lds_addr(vst) + gl * 1024);
+                    dma16s(kc_p + gb, kofs_g[i], ldsk);
+                    dma16s(vc_p + gb, vofs_g[i], ldsv);
+                }
+            }
+            return;
+        }
         int pages[4] = {0, 0, 0, 0};
         const int pfirst = __builtin_amdgcn_readfirstlane(start >> p.page_shift);
         if (SP && !is_tree) {
@@ -510,6 +567,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
         // pg0 holds the pages from the split's first key on; rows past kend
         // fall back to the block's first key, so only valid pages are used
         issue_dma(0, StageTag<0>(), StageTag<1>());
+        prefetch_pages(1);
     }
     // A tree-only unit of a request whose tree fits one 64-node block needs
     // that block whatever the mask words say (every row sees its own node),
@@ -670,6 +728,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     auto step = [&](int j, auto stage) {
         if (j + 1 < n_steps) {
             issue_dma(j + 1, StageTag<1 - decltype(stage)::value>(), StageTag<0>());   // overlaps the math below
+            prefetch_pages(j + 2);              // for the next step's issue
             if ((j + 2) * KSB <= n_blocks)
                 TA_WAIT_VMCNT(2 * NIW);         // this wave's step-j DMA has landed
             else
@@ -822,8 +881,11 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     // which does not see the DMA, then has no load of its own outstanding
     // inside the loop and inserts no waits there.
     TA_WAIT_VMCNT(0);
-    if (!early && !early_tree && n_steps > 0)
+    if (!early && !early_tree && n_steps > 0) {
+        prefetch_pages(0);
         issue_dma(0, StageTag<0>(), StageTag<0>());
+        prefetch_pages(1);
+    }
     for (int j = 0; j < n_steps; j += 2) {
         step(j, StageTag<0>());
         if (j + 1 < n_steps)
