@@ -36,6 +36,7 @@ static constexpr float kLn2 = 0.69314718055994530942f;
 // bf16 range, and the rescale (a multiply of the whole accumulator) is rare.
 static constexpr float kRescaleSlack = 8.0f;
 
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
@@ -723,21 +724,22 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     float l_run = 0.f;         // this half's partial sum of probabilities
     const float c2 = p.c2;
 
-    // one step: start the next step's DMA into the other stage, wait for
-    // this step's, then the math on this stage
+    // one step: wait for this step's DMA, one barrier (every wave's copy has
+    // landed and every wave has finished the step before), start the next
+    // step's DMA into the other stage, then the math on this stage.  One
+    // barrier per step suffices with two stages because the next copy is
+    // issued only after it.
     auto step = [&](int j, auto stage) {
-        if (j + 1 < n_steps) {
-            issue_dma(j + 1, StageTag<1 - decltype(stage)::value>(), StageTag<0>());   // overlaps the math below
-            prefetch_pages(j + 2);              // for the next step's issue
-            if ((j + 2) * KSB <= n_blocks)
-                TA_WAIT_VMCNT(2 * NIW);         // this wave's step-j DMA has landed
-            else
-                TA_WAIT_VMCNT(0);               // the next step is partial: its count differs
-        } else {
-            TA_WAIT_VMCNT(0);
-        }
+        TA_WAIT_VMCNT(0);                       // this wave's step-j DMA has landed
+        __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): its LDS reads of step j-1 are done
+        asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();           // ... and every other wave's too
-        asm volatile("" ::: "memory");          // no LDS read moves above it
+        asm volatile("" ::: "memory");          // no LDS access moves across it
+        if (j + 1 < n_steps) {
+            // the other stage was last read in step j-1, which every wave has left
+            issue_dma(j + 1, StageTag<1 - decltype(stage)::value>(), StageTag<0>());
+            prefetch_pages(j + 2);
+        }
         const int k = j * KSB + my_blk;
         if (k < n_blocks) {
             bool is_tree;
@@ -871,10 +873,6 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
                 }
             }
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS reads are done
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();         // the stage may now be overwritten
-        asm volatile("" ::: "memory");
     };
 
     // Q and mask words are in registers before the loop: the compiler,
@@ -891,6 +889,14 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
         if (j + 1 < n_steps)
             step(j + 1, StageTag<1>());
     }
+    if (KS > 1) {
+        // the slice combine below reuses the stages: every wave must be done
+        // reading them
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    }
 
     float l_tot = l_run + __shfl_xor(l_run, 32);
     float m_fin = m_run;
@@ -899,7 +905,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     if (KS > 1) {
         // Combine the key slices of each row tile.  Every wave publishes its
         // rows' (max, sum) and the output tiles it does not own; the stages
-        // are free after the loop's last barrier.
+        // are free after the barrier above.
         float *xo = (float *)kv_lds;   // [NR][KS][NDT - NDT/KS][32 x 32] fp32, lane-major
         constexpr int NX = NDT - NDT / KS;
         static_assert(NR * KS * NX * 4096 <= 4 * SBYTES, "combine buffer exceeds the stages");
