@@ -156,7 +156,13 @@ size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
  *   anc_mask    [N, TREE_ATTN_MASK_WORDS] u64, as written by tree_attn_plan
  *   out         [N, Hq, D] dtype;  lse [N, Hq] f32
  *   workspace   tree_attn_workspace_bytes(...) bytes, 256-byte aligned, or
- *               NULL when that is 0; its contents are scratch between calls
+ *               NULL when that is 0; its contents are scratch between calls.
+ *               With more than one split (bf16 only) it holds each split's
+ *               normalised partial output in fp16 ([splits, N, Hq, D]) and its
+ *               partial log-sum-exp in fp32 ([splits, N, Hq]).  A normalised
+ *               partial is a convex combination of V rows, so fp16 keeps it
+ *               to 2^-11 relative as long as every |V| entry is below 65504,
+ *               the fp16 range: a precondition of split calls.
  * Host sizes: max_tree >= every T_b (<= 256), max_prefix >= every
  *   prefix_len[b] (<= max_pages_per_seq * page_size).  They size the launch
  *   so no call ever reads device data on the host.

@@ -216,7 +216,8 @@ def test_split_choice_properties():
                 if s == 1:
                     assert ws == 0
                 else:
-                    assert ws >= s * B * T * 16 * (128 + 1) * 4
+                    # fp16 partial outputs and fp32 partial lse per split
+                    assert ws >= s * B * T * 16 * (128 * 2 + 4)
     # forcing a split count, and no workspace without a prefix
     assert ta.workspace_bytes(1, 16, 32, 8, 128, 16, 2048, num_splits=3) > 0
     assert ta.workspace_bytes(1, 16, 32, 8, 128, 16, 0) == 0

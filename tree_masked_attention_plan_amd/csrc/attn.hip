@@ -27,6 +27,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));   // split partial outputs
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -1005,9 +1006,9 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
                 continue;
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                const f32x4 v = {acc_o[dt][i4 * 4 + 0] * inv, acc_o[dt][i4 * 4 + 1] * inv,
-                                 acc_o[dt][i4 * 4 + 2] * inv, acc_o[dt][i4 * 4 + 3] * inv};
-                *(__attribute__((address_space(1))) f32x4 *)(orow + dt * 32 + i4 * 8 + hh * 4) = v;
+                const f16x4 v = {(_Float16)(acc_o[dt][i4 * 4 + 0] * inv), (_Float16)(acc_o[dt][i4 * 4 + 1] * inv),
+                                 (_Float16)(acc_o[dt][i4 * 4 + 2] * inv), (_Float16)(acc_o[dt][i4 * 4 + 3] * inv)};
+                *(__attribute__((address_space(1))) f16x4 *)(orow + dt * 32 + i4 * 8 + hh * 4) = v;
             }
         }
         if (lse_writer)
@@ -1020,7 +1021,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
 //   lse = log2 sum_s 2^{lse_s};  O = sum_s 2^{lse_s - lse} O_s
 // Every split slot holds an lse for every row (-inf for an empty prefix
 // split), so the merge needs no request geometry.  A split's partial row is D
-// fp32 values, read as float4 by D/4 lanes, so one wave-wide load covers
+// fp16 values, read four at a time by D/4 lanes, so one wave-wide load covers
 // SPI = 256/D splits; the lse and all partial loads of a batch are issued
 // before any is used (one memory latency per 16 * SPI splits).  Partial rows
 // of zero-weight splits may hold stale data and are excluded by a select.
@@ -1032,7 +1033,8 @@ __global__ __launch_bounds__(256) void merge_kernel(FwdParams p)
     constexpr int SPI = 64 / LPS;     // splits per wave-wide load
     constexpr int BATCH = 16;         // loads in flight per lane
     // the few arguments used, loaded together (opaque copies, as load_args)
-    const float *ws_o = p.ws_o, *ws_lse = p.ws_lse;
+    const _Float16 *ws_o = p.ws_o;
+    const float *ws_lse = p.ws_lse;
     void *out = p.out;
     float *lse_out = p.lse;
     int N = p.N, Hq = p.Hq, ns = p.nsplit;
@@ -1044,16 +1046,16 @@ __global__ __launch_bounds__(256) void merge_kernel(FwdParams p)
     const int64_t split_stride = (int64_t)N * Hq;   // rows between splits
     const int grp = lane / LPS;       // which split of a load this lane takes
     const int dcol = (lane % LPS) * 4;
-    const float *src = ws_o + r0 * D + dcol;
+    const _Float16 *src = ws_o + r0 * D + dcol;
 
     // The whole first batch and the lse are in flight before anything waits:
     // partial rows first, the lse last (vmcnt counts in issue order).  Loads
     // are unconditional, of a clamped slot, so that no branch separates them;
     // a slot past the end is dropped by the weighting below.
     auto load = [&](int s) {
-        return *(const __attribute__((address_space(1))) f32x4 *)(src + min(s, ns - 1) * split_stride * D);
+        return *(const __attribute__((address_space(1))) f16x4 *)(src + min(s, ns - 1) * split_stride * D);
     };
-    f32x4 v[BATCH];
+    f16x4 v[BATCH];
 #pragma unroll
     for (int i = 0; i < BATCH; ++i)
         v[i] = load(i * SPI + grp);
@@ -1073,13 +1075,13 @@ __global__ __launch_bounds__(256) void merge_kernel(FwdParams p)
         tot += __shfl_xor(tot, o);
 
     float4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto add = [&](const f32x4 &x, int s) {
+    auto add = [&](const f16x4 &x, int s) {
         const float ws = __shfl(wgt, s & 63);
         if (s < ns && ws > 0.f) {
-            acc.x += ws * x.x;
-            acc.y += ws * x.y;
-            acc.z += ws * x.z;
-            acc.w += ws * x.w;
+            acc.x += ws * (float)x[0];
+            acc.y += ws * (float)x[1];
+            acc.z += ws * (float)x[2];
+            acc.w += ws * (float)x[3];
         }
     };
 #pragma unroll

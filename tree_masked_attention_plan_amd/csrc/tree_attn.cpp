@@ -139,9 +139,11 @@ Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tre
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// A split's partial output is normalised (a convex combination of V rows),
+// so fp16 holds it to 2^-11 relative; the partial lse stays fp32.
 size_t ws_o_bytes(int32_t nsplit, int32_t N, int32_t Hq, int32_t D)
 {
-    return align256((size_t)nsplit * N * Hq * D * sizeof(float));
+    return align256((size_t)nsplit * N * Hq * D * sizeof(_Float16));
 }
 
 size_t ws_bytes(const Geometry &g, int32_t N, int32_t Hq, int32_t D)
@@ -465,7 +467,7 @@ ta_status_t run_fwd(const void *q, const void *k_tree, const void *v_tree, const
     p.ws_o = nullptr;
     p.ws_lse = nullptr;
     if (g.nsplit > 1) {
-        p.ws_o = (float *)workspace;
+        p.ws_o = (_Float16 *)workspace;
         p.ws_lse = (float *)((char *)workspace + ws_o_bytes(g.nsplit, N, Hq, D));
     }
     p.B = B;
