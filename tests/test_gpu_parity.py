@@ -176,6 +176,13 @@ def small_cases():
         # enough (request, kv head, 128-row) units for the 4-wave workgroups
         ("wide-batch", [int(x) for x in rng.integers(1, 400, 16)],
          [W.best_first_tree(64, rng) for _ in range(16)], dict(Hq=32, Hkv=8)),
+        # <= 32 rows per kv head with long prefixes: one row tile, so a wave's
+        # copy rows of a full prefix block span two 16-row page groups
+        # (head_dim 128: four key slices; head_dim 64: two)
+        ("few-rows-long-prefix", [1000, 613], [W.chain(5), W.best_first_tree(7, rng)], {}),
+        ("d64-few-rows-long-prefix", [1500], [W.chain(6)], dict(D=64)),
+        # pages of 32 tokens: two 16-row groups per page
+        ("page32-long-prefix", [2000, 77], [W.best_first_tree(64, rng), W.chain(4)], dict(ps=32)),
     ]
     return cases
 
