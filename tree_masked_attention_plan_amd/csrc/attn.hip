@@ -1023,15 +1023,15 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
 // split), so the merge needs no request geometry.  A split's partial row is D
 // fp16 values, read four at a time by D/4 lanes, so one wave-wide load covers
 // SPI = 256/D splits; the lse and all partial loads of a batch are issued
-// before any is used (one memory latency per 16 * SPI splits).  Partial rows
+// before any is used (one memory latency per BATCH * SPI splits).  Partial rows
 // of zero-weight splits may hold stale data and are excluded by a select.
 // ---------------------------------------------------------------------------
-template <int D, typename OutT>
+template <int D, typename OutT, int BATCH>
 __global__ __launch_bounds__(256) void merge_kernel(FwdParams p)
 {
     constexpr int LPS = D / 4;        // lanes per split row
     constexpr int SPI = 64 / LPS;     // splits per wave-wide load
-    constexpr int BATCH = 16;         // loads in flight per lane
+    // BATCH: loads in flight per lane, sized by the host to the split count
     // the few arguments used, loaded together (opaque copies, as load_args)
     const _Float16 *ws_o = p.ws_o;
     const float *ws_lse = p.ws_lse;
@@ -1263,10 +1263,25 @@ hipError_t launch_merge(const FwdParams &p, hipStream_t stream)
     if (p.nsplit == 1)
         return hipSuccess;
     const dim3 grid((unsigned)(((int64_t)p.N * p.Hq + 3) / 4));
-    if (p.D == 64)
-        hipLaunchKernelGGL((merge_kernel<64, __bf16>), grid, dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL((merge_kernel<128, __bf16>), grid, dim3(256), 0, stream, p);
+    // one batch of loads covers BATCH * (256 / D) splits; the smallest batch
+    // that covers every split saves loads of the clamped last slot
+    const int spi = 256 / p.D;
+    const int need = (p.nsplit + spi - 1) / spi;
+    if (p.D == 64) {
+        if (need <= 4)
+            hipLaunchKernelGGL((merge_kernel<64, __bf16, 4>), grid, dim3(256), 0, stream, p);
+        else if (need <= 8)
+            hipLaunchKernelGGL((merge_kernel<64, __bf16, 8>), grid, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((merge_kernel<64, __bf16, 16>), grid, dim3(256), 0, stream, p);
+    } else {
+        if (need <= 4)
+            hipLaunchKernelGGL((merge_kernel<128, __bf16, 4>), grid, dim3(256), 0, stream, p);
+        else if (need <= 8)
+            hipLaunchKernelGGL((merge_kernel<128, __bf16, 8>), grid, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((merge_kernel<128, __bf16, 16>), grid, dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
