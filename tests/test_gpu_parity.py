@@ -222,6 +222,24 @@ def test_large_and_jumping_scores(dev, dtype):
         assert_close(w, out, lse, o_ref, l_ref, f"rescale {dtype} splits={ns}")
 
 
+def test_large_values_through_fp16_partials(dev):
+    """Split calls keep each split's normalised partial output in fp16.  A
+    partial is a convex combination of V rows, so it stays within the fp16
+    range when every |V| does: V scaled by 2^13 (|V| up to about 4e4, exact
+    in bf16) still matches the oracle, compared in units of the scale."""
+    rng = W.rng_for(23, 0)
+    w = small("large-v", [1500, 300], [W.chain(16), W.best_first_tree(40, rng)], seed=23)
+    scale = 2.0 ** 13
+    w.v_cache = (w.v_cache.float() * scale).to(torch.bfloat16)    # sentinel NaN slots stay NaN
+    w.v_tree = (w.v_tree.float() * scale).to(torch.bfloat16)
+    vmax = max(torch.nan_to_num(w.v_cache.float()).abs().max().item(), w.v_tree.float().abs().max().item())
+    assert 2.0 ** 14 < vmax < 65504.0
+    o_ref, l_ref = oracle.tree_attn_workload(w)
+    for ns in (0, 5, 17, 64):
+        out, lse = gpu_fwd(w, dev, num_splits=ns)
+        assert_close(w, out / scale, lse, np.asarray(o_ref) / scale, l_ref, f"large-v splits={ns}")
+
+
 def test_softmax_scale_override(dev):
     rng = W.rng_for(8, 0)
     w = small("scale", [90], [W.best_first_tree(30, rng)], seed=8)
