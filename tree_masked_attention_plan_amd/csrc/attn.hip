@@ -37,7 +37,6 @@ static constexpr float kLn2 = 0.69314718055994530942f;
 // bf16 range, and the rescale (a multiply of the whole accumulator) is rare.
 static constexpr float kRescaleSlack = 8.0f;
 
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
@@ -437,11 +436,12 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
         }
     };
 
-    // Issue this wave's copies of step j into a stage.  Page ids are fetched
-    // so that no vector load sits between two steps' DMA batches (the vmcnt
-    // waits below count DMA instructions only): with SP they come from scalar
-    // loads (or from pg0, for the split's first step); smaller pages use
-    // per-lane loads, consumed before the DMA is issued.
+    // Issue this wave's copies of step j into a stage.  Page ids never come
+    // from vector loads left in flight (the loop's vmcnt waits count DMA
+    // instructions only): with SP a full block uses the ids prefetched a step
+    // ahead (pf_pg), the split's first step those read into pg0, and a ragged
+    // block scalar loads; smaller pages use per-lane loads, consumed before
+    // the DMA is issued.
     // FIRST: the split's first step, whose page ids were read into pg0
     auto issue_dma = [&](int j, auto stage, auto first) {
         constexpr bool FIRST = decltype(first)::value != 0;
