@@ -302,6 +302,36 @@ def test_non_ancestors_do_not_leak():
             assert not np.array_equal(o1[i], o3[i])
 
 
+def test_lse_merge_of_prefix_halves():
+    """The split-K merge rule on oracle outputs.  Every row sees its root
+    path, so runs over the first half of the prefix (A) and the second half
+    (B) both hold the tree; a run with no prefix (C) removes the double count:
+    e^lse = e^lse_A + e^lse_B - e^lse_C and O e^lse = O_A e^lse_A +
+    O_B e^lse_B - O_C e^lse_C, to fp64 rounding.  This pins lse as the natural
+    log of the row's exp-sum and O as the normalised weighted sum."""
+    rng = W.rng_for(29, 0)
+    trees = [W.best_first_tree(24, rng), W.random_tree(17, 5, rng)]
+    w = small_workload([200, 75], trees, seed=29)
+    ps = w.page_size
+    o_f, l_f = oracle.tree_attn_workload(w)
+    half = torch.tensor([(int(L) // (2 * ps)) * ps for L in w.prefix_len], dtype=torch.int32)
+    bt_b = torch.full_like(w.block_table, -1)
+    for b in range(w.B):
+        skip = int(half[b]) // ps
+        bt_b[b, :w.max_pages - skip] = w.block_table[b, skip:]
+    run = lambda bt, L: oracle.tree_attn(w.q, w.k_tree, w.v_tree, w.k_cache, w.v_cache, bt, L,
+                                        w.tree_off, w.parent, scale=w.scale)
+    o_a, l_a = run(w.block_table, half)
+    o_b, l_b = run(bt_b, w.prefix_len - half)
+    o_c, l_c = run(w.block_table, torch.zeros_like(w.prefix_len))
+    m = np.maximum(np.maximum(l_a, l_b), l_c)
+    ea, eb, ec = np.exp(l_a - m), np.exp(l_b - m), np.exp(l_c - m)
+    tot = ea + eb - ec
+    np.testing.assert_allclose(np.log(tot) + m, l_f, rtol=0, atol=1e-12)
+    merged = (o_a * ea[..., None] + o_b * eb[..., None] - o_c * ec[..., None]) / tot[..., None]
+    np.testing.assert_allclose(merged, o_f, rtol=0, atol=1e-11)
+
+
 def test_zero_keys_closed_form():
     rng = W.rng_for(17, 0)
     trees = [W.random_tree(30, 6, rng), W.chain(4)]
