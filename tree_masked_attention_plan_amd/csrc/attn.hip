@@ -652,16 +652,37 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
                 __syncthreads();
                 req_status = first_bad_l + 1;
             }
+            // Trees of up to 64 nodes: one node per lane, and the ancestor
+            // sets by pointer jumping.  Lane l holds the nodes from l up to,
+            // not including, jp (its first ancestor not yet merged); each
+            // round merges jp's set and jumps to jp's jp, so a path of depth
+            // d needs about log2(d) rounds of cross-lane reads, where walking
+            // it costs d dependent LDS reads.  Each row then takes its node's
+            // word from the lane that holds it.
+            uint64_t wrow = 0;
+            if (req_status == kTreeOk && R.T <= 64) {   // uniform
+                int jp = lane < R.T ? par_l[lane] : -1;
+                uint64_t m = lane < R.T ? (1ull << lane) : 0ull;
+                while (__ballot(jp >= 0) != 0ull) {     // ends: parents precede children
+                    const int src = jp >= 0 ? jp : lane;
+                    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)m, src);
+                    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(m >> 32), src);
+                    const int jj = __shfl(jp, src);
+                    if (jp >= 0) {
+                        m |= ((uint64_t)hi << 32) | lo;
+                        jp = jj;
+                    }
+                }
+                const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)m, node);
+                const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(m >> 32), node);
+                wrow = ((uint64_t)hi << 32) | lo;
+            }
             if (req_status == kTreeOk && row_ok) {
                 uint64_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
                 int d = 0;
                 if (R.T <= 64) {
-                    // one mask word: the shortest loop (the walk's steps are
-                    // dependent LDS reads)
-                    for (int a = node; a >= 0; a = par_l[a]) {
-                        w0 |= 1ull << a;
-                        ++d;
-                    }
+                    w0 = wrow;
+                    d = __builtin_popcountll(wrow);
                 } else {
                     for (int a = node; a >= 0; a = par_l[a]) {
                         const uint64_t bit = 1ull << (a & 63);
