@@ -614,13 +614,64 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     };
 
     uint64_t mw[kMaskWords] = {0, 0, 0, 0};
-    if (R.owns_tree) {
+    if (R.owns_tree && fuse && R.T <= 64) {
+        // The plan of a tree of up to 64 nodes, in every wave on its own (no
+        // workgroup barrier): lane l loads node l's parent, a ballot finds the
+        // first bad parent (parent[j] outside [-1, j)), and the ancestor sets
+        // come by pointer jumping.  Lane l holds the nodes from l up to, not
+        // including, jp (its first ancestor not yet merged); each round merges
+        // jp's set and jumps to jp's jp, so a path of depth d needs about
+        // log2(d) rounds of cross-lane reads where walking it costs d
+        // dependent loads.  Each row then takes its node's word from the lane
+        // that holds it.  Units of kv head 0 write the plan's outputs: one
+        // row per node (its group's first q head) and, from row tile 0, the
+        // request's status.
+        int jp = -1;
+        if (req_status == kTreeOk && lane < R.T)
+            jp = gmem(p.parent)[R.off + lane];
+        const uint64_t bad = __ballot(lane < R.T && (jp < -1 || jp >= lane));
+        if (req_status == kTreeOk && bad != 0ull)
+            req_status = __builtin_ctzll(bad) + 1;   // uniform: every wave reads the same parents
+        if (req_status == kTreeOk) {
+            uint64_t m = lane < R.T ? (1ull << lane) : 0ull;
+            while (__ballot(jp >= 0) != 0ull) {      // ends: parents precede children
+                const int src = jp >= 0 ? jp : lane;
+                const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)m, src);
+                const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(m >> 32), src);
+                const int jj = __shfl(jp, src);
+                if (jp >= 0) {
+                    m |= ((uint64_t)hi << 32) | lo;
+                    jp = jj;
+                }
+            }
+            const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)m, node);
+            const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(m >> 32), node);
+            const uint64_t wrow = ((uint64_t)hi << 32) | lo;
+            if (row_ok) {
+                mw[0] = wrow;
+                if (c == 0 && hh == 0 && ks == 0 && my_row == node * p.G) {
+                    const int64_t n = R.off + node;
+                    const int d = __builtin_popcountll(wrow);
+                    const auto mrow = gmem(p.plan_mask) + n * kMaskWords;
+                    mrow[0] = wrow;
+                    mrow[1] = 0ull;
+                    mrow[2] = 0ull;
+                    mrow[3] = 0ull;
+                    gmem(p.plan_depth)[n] = d;
+                    gmem(p.plan_pos)[n] = L_raw + d - 1;
+                }
+            }
+            // every row sees its own node, all in the first 64-node block
+            tree_need |= 1;
+        }
+        if (c == 0 && u.rt == 0 && tid == 0)
+            gmem(p.plan_status)[u.b] = req_status;
+    } else if (R.owns_tree) {
         if (fuse) {
-            // Stage the request's parents and check them as the plan does
-            // (parent[j] in [-1, j)); then each row walks its node's parent
-            // chain, which ends within node + 1 steps.  Units of kv head 0
-            // write the plan's outputs: one row per node (its group's first
-            // q head) and, from row tile 0, the request's status.
+            // Larger trees: stage the request's parents in LDS and check them
+            // as the plan does (parent[j] in [-1, j)); then each row walks its
+            // node's parent chain, which ends within node + 1 steps.  Outputs
+            // as above.
             constexpr int NPT = (kMaxTree + NW * 64 - 1) / (NW * 64);   // parents per thread
             uint32_t badp = 0;
             if (req_status == kTreeOk) {
@@ -652,47 +703,17 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
                 __syncthreads();
                 req_status = first_bad_l + 1;
             }
-            // Trees of up to 64 nodes: one node per lane, and the ancestor
-            // sets by pointer jumping.  Lane l holds the nodes from l up to,
-            // not including, jp (its first ancestor not yet merged); each
-            // round merges jp's set and jumps to jp's jp, so a path of depth
-            // d needs about log2(d) rounds of cross-lane reads, where walking
-            // it costs d dependent LDS reads.  Each row then takes its node's
-            // word from the lane that holds it.
-            uint64_t wrow = 0;
-            if (req_status == kTreeOk && R.T <= 64) {   // uniform
-                int jp = lane < R.T ? par_l[lane] : -1;
-                uint64_t m = lane < R.T ? (1ull << lane) : 0ull;
-                while (__ballot(jp >= 0) != 0ull) {     // ends: parents precede children
-                    const int src = jp >= 0 ? jp : lane;
-                    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)m, src);
-                    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(m >> 32), src);
-                    const int jj = __shfl(jp, src);
-                    if (jp >= 0) {
-                        m |= ((uint64_t)hi << 32) | lo;
-                        jp = jj;
-                    }
-                }
-                const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)m, node);
-                const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(m >> 32), node);
-                wrow = ((uint64_t)hi << 32) | lo;
-            }
             if (req_status == kTreeOk && row_ok) {
                 uint64_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
                 int d = 0;
-                if (R.T <= 64) {
-                    w0 = wrow;
-                    d = __builtin_popcountll(wrow);
-                } else {
-                    for (int a = node; a >= 0; a = par_l[a]) {
-                        const uint64_t bit = 1ull << (a & 63);
-                        const int word = a >> 6;
-                        w0 |= word == 0 ? bit : 0ull;
-                        w1 |= word == 1 ? bit : 0ull;
-                        w2 |= word == 2 ? bit : 0ull;
-                        w3 |= word == 3 ? bit : 0ull;
-                        ++d;
-                    }
+                for (int a = node; a >= 0; a = par_l[a]) {
+                    const uint64_t bit = 1ull << (a & 63);
+                    const int word = a >> 6;
+                    w0 |= word == 0 ? bit : 0ull;
+                    w1 |= word == 1 ? bit : 0ull;
+                    w2 |= word == 2 ? bit : 0ull;
+                    w3 |= word == 3 ? bit : 0ull;
+                    ++d;
                 }
                 mw[0] = w0;
                 mw[1] = w1;
