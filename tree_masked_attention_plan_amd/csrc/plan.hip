@@ -46,6 +46,47 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p_arg)
             gmem(p.status)[b] = bad_off ? kTreeBadOffsets : kTreeBadPrefix;
         return;
     }
+    if (T <= 64) {
+        // A tree of up to 64 nodes fits one wave: lane j holds node j, a
+        // ballot finds the first bad parent, and the ancestor sets come by
+        // pointer jumping (each round merges the set of the lane's next
+        // unmerged ancestor and jumps past it: about log2(depth) rounds of
+        // cross-lane reads instead of depth dependent LDS reads).  The other
+        // waves have nothing to do.
+        if (j >= 64)
+            return;   // whole waves
+        int32_t jp = j < T ? gmem(p.parent)[off + j] : -1;
+        const uint64_t bad = __ballot(j < T && (jp < -1 || jp >= j));
+        if (bad != 0ull) {
+            if (j == 0)
+                gmem(p.status)[b] = (int32_t)__builtin_ctzll(bad) + 1;
+            return;
+        }
+        uint64_t m = j < T ? (1ull << j) : 0ull;
+        while (__ballot(jp >= 0) != 0ull) {   // ends: parents precede children
+            const int src = jp >= 0 ? jp : j;
+            const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)m, src);
+            const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(m >> 32), src);
+            const int32_t jj = __shfl(jp, src);
+            if (jp >= 0) {
+                m |= ((uint64_t)hi << 32) | lo;
+                jp = jj;
+            }
+        }
+        if (j < T) {
+            const int32_t d = __builtin_popcountll(m);
+            __attribute__((address_space(1))) uint64_t *row = gmem(p.anc_mask) + (int64_t)(off + j) * kMaskWords;
+            row[0] = m;
+            row[1] = 0;
+            row[2] = 0;
+            row[3] = 0;
+            gmem(p.depth)[off + j] = d;
+            gmem(p.pos_id)[off + j] = L + d - 1;
+        }
+        if (j == 0)
+            gmem(p.status)[b] = kTreeOk;
+        return;
+    }
     if (j == 0)
         first_bad = INT32_MAX;
     int32_t pj = -1;
