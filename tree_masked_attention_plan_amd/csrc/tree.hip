@@ -9,22 +9,25 @@
 namespace ta {
 
 // ---------------------------------------------------------------------------
-// best-first draft trees: one wave per request.  Candidate slot e is the e-th
-// push (the root's children are 0..K-1, node i's children K + K*i .. +K-1),
-// so the slot index is also the tie-break key, and the candidate's parent and
-// token follow from it.  Slots are grouped in chunks of 64 whose best
-// candidate is kept in LDS (a two-level tournament): a pop is a wave-wide
-// argmax over the chunk bests, and afterwards only the chunks that changed
-// (the popped slot's, and the one or two the new children land in) are
-// re-reduced, one slot per lane.  Scores are the same fp32 sums, in the same
-// order, as in the sequential definition, so every comparison is decided
-// identically.
+// best-first draft trees: one wave per request.
+//
+// Push numbers follow the sequential definition: the root's children are
+// 0..K-1 and node i's children K + K*i .. +K-1, so the push number is the
+// tie-break key and the candidate's parent and token follow from it.
+//
+// Every child of a node is pushed when the node is popped, and the children
+// of one parent leave the pool in the pop order, (score desc, push number
+// asc).  So at any time only the best not-yet-popped child of each popped
+// node can be the next pop.  The pool holds just that one representative per
+// parent: a pop removes the winner w, adds w's next sibling in its parent's
+// order (the best sibling whose key is below w's) and w's own best child.
+// The pop sequence, and with it every output, is that of the full
+// expansion, with at most T + 1 live candidates.  Scores are the same fp32
+// sums, in the same order, so every comparison is decided identically.
+//
+// The pool sits in registers, a few 64-bit keys per lane; a pop is a
+// per-lane max and one wave-wide max.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool cand_better(float sa, int ea, float sb, int eb)
-{
-    return sa > sb || (sa == sb && ea < eb);
-}
-
 // A candidate as one 64-bit key whose unsigned order is the pop order:
 // larger score first (the float's bits mapped to an order-preserving
 // unsigned), then smaller slot.  Key 0 is "no candidate" (also NaN scores,
@@ -68,135 +71,133 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)
     return ((uint64_t)hi << 32) | lo;
 }
 
-// wave-wide best of (s, e) pairs; every lane gets the result.  DPP rotations
-// inside each row of 16 lanes (row_ror 1, 2, 4, 8), then the four row maxima
-// through readlane: a few cycles per step, no LDS round trips.
-__device__ __forceinline__ void wave_best(float &s, int &e)
+// max of 64-bit keys inside each row of 16 lanes: every lane of a row gets
+// its row's max (DPP rotations)
+__device__ __forceinline__ uint64_t row_max_key(uint64_t k)
 {
-    uint64_t k = cand_key(s, e);
     uint64_t o;
     o = dpp_u64<0x121>(k); k = o > k ? o : k;   // row_ror:1
     o = dpp_u64<0x122>(k); k = o > k ? o : k;   // row_ror:2
     o = dpp_u64<0x124>(k); k = o > k ? o : k;   // row_ror:4
     o = dpp_u64<0x128>(k); k = o > k ? o : k;   // row_ror:8
+    return k;
+}
+
+// wave-wide max of 64-bit keys; every lane gets the result (the row maxima,
+// then the four of them through readlane)
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k)
+{
+    k = row_max_key(k);
     const uint64_t r0 = readlane_u64(k, 0), r1 = readlane_u64(k, 16);
     const uint64_t r2 = readlane_u64(k, 32), r3 = readlane_u64(k, 48);
     const uint64_t a = r0 > r1 ? r0 : r1, c = r2 > r3 ? r2 : r3;
-    cand_of_key(a > c ? a : c, s, e);
+    return a > c ? a : c;
 }
 
 __global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p)
 {
-    constexpr int kChunks = (kTreeMaxPool + 63) / 64;
-    // candidate scores; NaN marks a slot that is empty or already popped (NaN
-    // never compares better, while -inf is a real score: probability 0)
-    __shared__ float pool[kTreeMaxPool];
-    __shared__ float cbest_s[kChunks];       // best candidate of each 64-slot chunk
-    __shared__ int32_t cbest_e[kChunks];
+    // pool positions: one per pop plus the root's first child
+    constexpr int NS = (kMaxTree + 1 + 63) / 64;
     __shared__ float lps[kTreeMaxLogp];      // this request's log-probabilities
+    __shared__ float node_score[kMaxTree];
     __shared__ int32_t node_depth[kMaxTree];
-    // outputs are staged here and written once at the end: a global store in
-    // the loop would make every pop's barrier wait for a memory round trip
+    // outputs are staged here and written once at the end
     __shared__ int32_t o_parent[kMaxTree], o_choice[kMaxTree];
-    __shared__ float o_score[kMaxTree];
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
     const int K = p.K, T = p.T, Dmax = p.Dmax;
-    const int cap = K * (T + 1);
-    const int nchunks = (cap + 63) / 64;
     const float kEmpty = __builtin_nanf("");
     const float *lp = p.logp + (int64_t)b * Dmax * K;
     for (int i = lane; i < Dmax * K; i += 64)
         lps[i] = lp[i];
-    for (int e = lane; e < cap; e += 64)
-        pool[e] = kEmpty;
-    for (int c = lane; c < nchunks; c += 64) {
-        cbest_s[c] = -INFINITY;
-        cbest_e[c] = INT32_MAX;
-    }
-    __syncthreads();
-    // re-reduce chunk c from its slots (one per lane)
-    auto refresh = [&](int c) {
-        const int f = c * 64 + lane;
-        float fs = -INFINITY;
-        int fe = INT32_MAX;
-        if (f < cap) {
-            const float v = pool[f];
-            if (cand_better(v, f, fs, fe)) {
-                fs = v;
-                fe = f;
-            }
-        }
-        wave_best(fs, fe);
-        if (lane == 0) {
-            cbest_s[c] = fs;
-            cbest_e[c] = fe;
-        }
-    };
-    // the root's children
-    if (lane < K)
-        pool[lane] = lps[lane];
-    __syncthreads();
-    refresh(0);
-    if (K > 64)
-        refresh(1);
-    __syncthreads();
     for (int i = lane; i < T; i += 64) {
         o_parent[i] = -1;
         o_choice[i] = -1;
-        o_score[i] = kEmpty;
+        node_score[i] = kEmpty;
     }
     __syncthreads();
+    uint64_t slot[NS];
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+        slot[q] = 0ull;
+    // the root's best child opens the pool (key 0: no candidate)
+    const uint64_t root_first = wave_max_key(lane < K ? cand_key(lps[lane], lane) : 0ull);
+    if (lane == 0)
+        slot[0] = root_first;
+    int cnt = 1;   // pool positions used (uniform)
     for (int i = 0; i < T; ++i) {
-        // argmax over the chunk bests
-        float ws = -INFINITY;
-        int we = INT32_MAX;
-        for (int c = lane; c < nchunks; c += 64) {
-            const float cs = cbest_s[c];
-            const int ce = cbest_e[c];
-            if (cand_better(cs, ce, ws, we)) {
-                ws = cs;
-                we = ce;
-            }
-        }
-        wave_best(ws, we);
-        if (we == INT32_MAX)
+        uint64_t lb = slot[0];
+#pragma unroll
+        for (int q = 1; q < NS; ++q)
+            lb = slot[q] > lb ? slot[q] : lb;
+        const uint64_t kw = wave_max_key(lb);
+        if (kw == 0ull)
             break;   // no candidate left: only with NaN inputs (the host checks
                      // that the implicit tree holds T nodes); the remaining
                      // nodes keep parent -1, choice -1, score NaN
-        const int e = we;                         // uniform
+        float ws;
+        int e;
+        cand_of_key(kw, ws, e);                   // uniform
         const int par = e < K ? -1 : (e - K) / K;
         const int k = e < K ? e : (e - K) % K;
-        const int depth = par < 0 ? 1 : node_depth[par] + 1;
+        const float sp = par < 0 ? 0.f : node_score[par];
+        const int dp = par < 0 ? 0 : node_depth[par];
+        const int depth = dp + 1;
         if (lane == 0) {
             o_parent[i] = par;
             o_choice[i] = k;
-            o_score[i] = ws;
+            node_score[i] = ws;
             node_depth[i] = depth;
-            pool[e] = kEmpty;
         }
-        // node i pushes its K children (slots K + K*i + c)
-        const int e0 = K + K * i;
-        const bool push = depth < Dmax;
-        if (push && lane < K)
-            pool[e0 + lane] = ws + lps[depth * K + lane];
-        __syncthreads();
-        const int c_pop = e >> 6;
-        refresh(c_pop);
-        if (push) {
-            const int c0 = e0 >> 6, c1 = (e0 + K - 1) >> 6;
-            if (c0 != c_pop)
-                refresh(c0);
-            if (c1 != c0 && c1 != c_pop)
-                refresh(c1);
+        // w's next sibling: the best child of its parent whose key is below
+        // w's; and node i's best child, when it is below the depth limit.
+        // With K <= 16 the two searches share one pass: sibling candidates
+        // in lanes 0..15, child candidates in lanes 16..31.
+        uint64_t k_sib, k_child;
+        if (K <= 16) {
+            const int j = lane & 15;
+            uint64_t key = 0ull;
+            if (lane < 16 && j < K) {
+                const float v = lps[dp * K + j];
+                const uint64_t c = cand_key(par < 0 ? v : sp + v, (par < 0 ? 0 : K + K * par) + j);
+                key = c < kw ? c : 0ull;
+            } else if (lane < 32 && j < K && depth < Dmax) {
+                key = cand_key(ws + lps[depth * K + j], K + K * i + j);
+            }
+            key = row_max_key(key);
+            k_sib = readlane_u64(key, 0);
+            k_child = readlane_u64(key, 16);
+        } else {
+            uint64_t ks = 0ull;
+            if (lane < K) {
+                const float v = lps[dp * K + lane];
+                const uint64_t c = cand_key(par < 0 ? v : sp + v, (par < 0 ? 0 : K + K * par) + lane);
+                ks = c < kw ? c : 0ull;
+            }
+            uint64_t kc = 0ull;
+            if (depth < Dmax && lane < K)
+                kc = cand_key(ws + lps[depth * K + lane], K + K * i + lane);
+            k_sib = wave_max_key(ks);
+            k_child = wave_max_key(kc);
         }
-        __syncthreads();   // chunk bests and node_depth before the next pop reads them
+        // the sibling takes the winner's place; the child takes a new position
+#pragma unroll
+        for (int q = 0; q < NS; ++q)
+            slot[q] = slot[q] == kw ? k_sib : slot[q];
+        if (k_child != 0ull) {
+            const int pos_lane = cnt & 63, pos_q = cnt >> 6;
+#pragma unroll
+            for (int q = 0; q < NS; ++q)
+                slot[q] = (q == pos_q && lane == pos_lane) ? k_child : slot[q];
+            ++cnt;
+        }
+        __syncthreads();   // node i's score and depth before a later pop reads them
     }
     __syncthreads();
     for (int i = lane; i < T; i += 64) {
         p.parent[(int64_t)b * T + i] = o_parent[i];
         p.choice[(int64_t)b * T + i] = o_choice[i];
-        p.score[(int64_t)b * T + i] = o_score[i];
+        p.score[(int64_t)b * T + i] = node_score[i];
     }
 }
 
