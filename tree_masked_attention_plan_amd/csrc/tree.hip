@@ -140,6 +140,8 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p)
         cand_of_key(kw, ws, e);                   // uniform
         const int par = e < K ? -1 : (e - K) / K;
         const int k = e < K ? e : (e - K) % K;
+        // a node's score and depth were written by lane 0 of this wave in an
+        // earlier pop; the wave's LDS accesses complete in program order
         const float sp = par < 0 ? 0.f : node_score[par];
         const int dp = par < 0 ? 0 : node_depth[par];
         const int depth = dp + 1;
@@ -155,14 +157,21 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p)
         // in lanes 0..15, child candidates in lanes 16..31.
         uint64_t k_sib, k_child;
         if (K <= 16) {
+            // one LDS read for both searches: lanes 0..15 read the parent's
+            // row of log-probabilities, lanes 16..31 node i's
             const int j = lane & 15;
+            const bool sib = lane < 16;
+            const int row = sib ? dp : depth;
+            const bool live = lane < 32 && j < K && (sib || depth < Dmax);
+            const float v = live ? lps[row * K + j] : 0.f;
             uint64_t key = 0ull;
-            if (lane < 16 && j < K) {
-                const float v = lps[dp * K + j];
-                const uint64_t c = cand_key(par < 0 ? v : sp + v, (par < 0 ? 0 : K + K * par) + j);
-                key = c < kw ? c : 0ull;
-            } else if (lane < 32 && j < K && depth < Dmax) {
-                key = cand_key(ws + lps[depth * K + j], K + K * i + j);
+            if (live) {
+                if (sib) {
+                    const uint64_t c = cand_key(par < 0 ? v : sp + v, (par < 0 ? 0 : K + K * par) + j);
+                    key = c < kw ? c : 0ull;
+                } else {
+                    key = cand_key(ws + v, K + K * i + j);
+                }
             }
             key = row_max_key(key);
             k_sib = readlane_u64(key, 0);
@@ -191,7 +200,6 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p)
                 slot[q] = (q == pos_q && lane == pos_lane) ? k_child : slot[q];
             ++cnt;
         }
-        __syncthreads();   // node i's score and depth before a later pop reads them
     }
     __syncthreads();
     for (int i = lane; i < T; i += 64) {
