@@ -76,3 +76,39 @@ def test_gpu_trees_feed_the_plan(dev):
     assert st.tolist() == [0] * B and res.status.cpu().tolist() == [0] * B
     assert np.array_equal(res.depth.cpu().numpy(), depth)
     assert int(depth.max()) <= 16
+
+
+def test_nan_candidates_are_never_chosen(dev):
+    """NaN log-probabilities are never popped.  With enough finite candidates
+    left, the trees equal the oracle's on the same inputs with NaN replaced by
+    -inf (every pop is then finite, and -inf candidates are never reached)."""
+    rng = np.random.default_rng(17)
+    lp = logsoftmax(rng.normal(0, 2, size=(4, 16, 8)))
+    nan_at = rng.random(size=lp.shape) < 0.4
+    nan_at[..., 0] = False                     # every depth keeps finite candidates
+    lp_nan = np.where(nan_at, np.float32(np.nan), lp).astype(np.float32)
+    lp_inf = np.where(nan_at, np.float32(-np.inf), lp).astype(np.float32)
+    p_ref, c_ref, s_ref = oracle.build_tree(lp_inf, 256)
+    assert np.isfinite(s_ref).all()
+    p, c, s = ta.build_tree(torch.from_numpy(lp_nan).to(dev), 256)
+    torch.cuda.synchronize()
+    assert np.array_equal(p.cpu().numpy(), p_ref)
+    assert np.array_equal(c.cpu().numpy(), c_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.int32), s_ref.view(np.int32))
+
+
+def test_nan_candidates_can_leave_nodes_missing(dev):
+    """One finite candidate per depth and three depths: a chain of three
+    nodes, then no candidate is left; the rest are written as missing."""
+    K, Dmax, T = 4, 3, 10
+    lp = np.full((2, Dmax, K), np.float32(np.nan), dtype=np.float32)
+    lp[0, :, 2] = np.float32(-0.5)
+    lp[1, :, 0] = np.float32(-1.0)
+    p, c, s = ta.build_tree(torch.from_numpy(lp).to(dev), T)
+    torch.cuda.synchronize()
+    p, c, s = p.cpu().numpy(), c.cpu().numpy(), s.cpu().numpy()
+    assert p[:, :3].tolist() == [[-1, 0, 1], [-1, 0, 1]]
+    assert c[:, :3].tolist() == [[2, 2, 2], [0, 0, 0]]
+    np.testing.assert_array_equal(s[0, :3], np.float32([-0.5, -1.0, -1.5]))
+    np.testing.assert_array_equal(s[1, :3], np.float32([-1.0, -2.0, -3.0]))
+    assert (p[:, 3:] == -1).all() and (c[:, 3:] == -1).all() and np.isnan(s[:, 3:]).all()
