@@ -151,6 +151,7 @@ __global__ __launch_bounds__(256) void plan_dfs_kernel(PlanDfsParams p_arg)
     __shared__ int32_t rank[kMaxTree];
     __shared__ int32_t sz[kMaxTree];
     __shared__ int32_t es[kMaxTree];
+    __shared__ int32_t bucket[4][kMaxTree + 1];   // per wave: subtree sums by parent + 1
     __shared__ int32_t first_bad;
     const int b = blockIdx.x;
     const int j = threadIdx.x;
@@ -195,11 +196,28 @@ __global__ __launch_bounds__(256) void plan_dfs_kernel(PlanDfsParams p_arg)
         }
     }
     __syncthreads();
-    // earlier siblings' subtrees (all threads read the same s at once)
+    // Earlier siblings' subtrees, es[j] = sum of sz[s] over s < j with
+    // parent[s] = parent[j]: the siblings in earlier waves through per-wave
+    // sums by parent (bucket p + 1, LDS atomics), those in this wave through
+    // a scan of its lanes with readlane.
+    const int w = j >> 6, l = j & 63;
+    for (int q = j; q < 4 * (kMaxTree + 1); q += 256)
+        (&bucket[0][0])[q] = 0;
+    const int32_t szj = j < T ? sz[j] : 0;
+    const int32_t pkey = j < T ? pj : -2;   // never matches a real parent
+    __syncthreads();
+    if (j < T)
+        atomicAdd(&bucket[w][pj + 1], szj);
+    int32_t e = 0;
+    for (int s = 0; s < 64; ++s) {
+        const int32_t ps = __builtin_amdgcn_readlane(pkey, s);
+        const int32_t zs = __builtin_amdgcn_readlane(szj, s);
+        e += (s < l && ps == pkey) ? zs : 0;
+    }
+    __syncthreads();
     if (j < T) {
-        int32_t e = 0;
-        for (int32_t s = 0; s < j; ++s)
-            e += par[s] == pj ? sz[s] : 0;
+        for (int w2 = 0; w2 < w; ++w2)
+            e += bucket[w2][pj + 1];
         es[j] = e;
     }
     __syncthreads();
