@@ -11,9 +11,10 @@ namespace ta {
 // ---------------------------------------------------------------------------
 // best-first draft trees: one wave per request.
 //
-// Push numbers follow the sequential definition: the root's children are
-// 0..K-1 and node i's children K + K*i .. +K-1, so the push number is the
-// tie-break key and the candidate's parent and token follow from it.
+// Equal scores go to the earlier push.  In the sequential definition the
+// root's children are pushes 0..K-1 and node i's children K + K*i .. +K-1,
+// i.e. pushes are ordered by (parent + 1, token): that pair, with the
+// candidate's depth appended, is the tie-break tag (cand_tag).
 //
 // Every child of a node is pushed when the node is popped, and the children
 // of one parent leave the pool in the pop order, (score desc, push number
@@ -94,13 +95,21 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k)
     return a > c ? a : c;
 }
 
+// A candidate's tie-break tag: (parent + 1, k) in the order of the push
+// numbers (K + K*parent + k, root children k), which it replaces, with the
+// candidate's depth below them (tags are unique without it, so it never
+// decides an order): a pop reads parent, token and depth with shifts.
+__device__ __forceinline__ int cand_tag(int par, int k, int depth)
+{
+    return ((par + 1) << 14) | (k << 8) | depth;
+}
+
 __global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p)
 {
     // pool positions: one per pop plus the root's first child
     constexpr int NS = (kMaxTree + 1 + 63) / 64;
     __shared__ float lps[kTreeMaxLogp];      // this request's log-probabilities
     __shared__ float node_score[kMaxTree];
-    __shared__ int32_t node_depth[kMaxTree];
     // outputs are staged here and written once at the end
     __shared__ int32_t o_parent[kMaxTree], o_choice[kMaxTree];
     const int b = blockIdx.x;
@@ -121,7 +130,7 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p)
     for (int q = 0; q < NS; ++q)
         slot[q] = 0ull;
     // the root's best child opens the pool (key 0: no candidate)
-    const uint64_t root_first = wave_max_key(lane < K ? cand_key(lps[lane], lane) : 0ull);
+    const uint64_t root_first = wave_max_key(lane < K ? cand_key(lps[lane], cand_tag(-1, lane, 1)) : 0ull);
     if (lane == 0)
         slot[0] = root_first;
     int cnt = 1;   // pool positions used (uniform)
@@ -138,18 +147,17 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p)
         float ws;
         int e;
         cand_of_key(kw, ws, e);                   // uniform
-        const int par = e < K ? -1 : (e - K) / K;
-        const int k = e < K ? e : (e - K) % K;
-        // a node's score and depth were written by lane 0 of this wave in an
-        // earlier pop; the wave's LDS accesses complete in program order
+        const int par = (e >> 14) - 1;
+        const int k = (e >> 8) & 63;
+        const int depth = e & 255;
+        const int dp = depth - 1;
+        // a node's score was written by lane 0 of this wave in an earlier
+        // pop; the wave's LDS accesses complete in program order
         const float sp = par < 0 ? 0.f : node_score[par];
-        const int dp = par < 0 ? 0 : node_depth[par];
-        const int depth = dp + 1;
         if (lane == 0) {
             o_parent[i] = par;
             o_choice[i] = k;
             node_score[i] = ws;
-            node_depth[i] = depth;
         }
         // w's next sibling: the best child of its parent whose key is below
         // w's; and node i's best child, when it is below the depth limit.
@@ -167,10 +175,10 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p)
             uint64_t key = 0ull;
             if (live) {
                 if (sib) {
-                    const uint64_t c = cand_key(par < 0 ? v : sp + v, (par < 0 ? 0 : K + K * par) + j);
+                    const uint64_t c = cand_key(par < 0 ? v : sp + v, cand_tag(par, j, depth));
                     key = c < kw ? c : 0ull;
                 } else {
-                    key = cand_key(ws + v, K + K * i + j);
+                    key = cand_key(ws + v, cand_tag(i, j, depth + 1));
                 }
             }
             key = row_max_key(key);
@@ -180,12 +188,12 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p)
             uint64_t ks = 0ull;
             if (lane < K) {
                 const float v = lps[dp * K + lane];
-                const uint64_t c = cand_key(par < 0 ? v : sp + v, (par < 0 ? 0 : K + K * par) + lane);
+                const uint64_t c = cand_key(par < 0 ? v : sp + v, cand_tag(par, lane, depth));
                 ks = c < kw ? c : 0ull;
             }
             uint64_t kc = 0ull;
             if (depth < Dmax && lane < K)
-                kc = cand_key(ws + lps[depth * K + lane], K + K * i + lane);
+                kc = cand_key(ws + lps[depth * K + lane], cand_tag(i, lane, depth + 1));
             k_sib = wave_max_key(ks);
             k_child = wave_max_key(kc);
         }
