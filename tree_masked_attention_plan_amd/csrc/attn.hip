@@ -1300,30 +1300,49 @@ hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nr, int ks, hipStr
     return hipGetLastError();
 }
 
+template <int D, int BATCH>
+static void launch_merge_n(const FwdParams &p, dim3 grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((merge_kernel<D, __bf16, BATCH>), grid, dim3(256), 0, stream, p);
+}
+
+template <int D>
+static void launch_merge_batch(const FwdParams &p, int need, dim3 grid, hipStream_t stream)
+{
+    switch (need) {
+    case 1: launch_merge_n<D, 1>(p, grid, stream); break;
+    case 2: launch_merge_n<D, 2>(p, grid, stream); break;
+    case 3: launch_merge_n<D, 3>(p, grid, stream); break;
+    case 4: launch_merge_n<D, 4>(p, grid, stream); break;
+    case 5: launch_merge_n<D, 5>(p, grid, stream); break;
+    case 6: launch_merge_n<D, 6>(p, grid, stream); break;
+    case 7: launch_merge_n<D, 7>(p, grid, stream); break;
+    case 8: launch_merge_n<D, 8>(p, grid, stream); break;
+    case 9: launch_merge_n<D, 9>(p, grid, stream); break;
+    case 10: launch_merge_n<D, 10>(p, grid, stream); break;
+    case 11: launch_merge_n<D, 11>(p, grid, stream); break;
+    case 12: launch_merge_n<D, 12>(p, grid, stream); break;
+    case 13: launch_merge_n<D, 13>(p, grid, stream); break;
+    case 14: launch_merge_n<D, 14>(p, grid, stream); break;
+    case 15: launch_merge_n<D, 15>(p, grid, stream); break;
+    default: launch_merge_n<D, 16>(p, grid, stream); break;
+    }
+}
+
 hipError_t launch_merge(const FwdParams &p, hipStream_t stream)
 {
     if (p.nsplit == 1)
         return hipSuccess;
     const dim3 grid((unsigned)(((int64_t)p.N * p.Hq + 3) / 4));
-    // one batch of loads covers BATCH * (256 / D) splits; the smallest batch
-    // that covers every split saves loads of the clamped last slot
+    // one batch of loads covers BATCH * (256 / D) splits: the smallest batch
+    // that covers the call's slots (at most 16; more slots take further
+    // batches), so that no lane loads clamped copies of the last slot
     const int spi = 256 / p.D;
-    const int need = (p.nsplit + spi - 1) / spi;
-    if (p.D == 64) {
-        if (need <= 4)
-            hipLaunchKernelGGL((merge_kernel<64, __bf16, 4>), grid, dim3(256), 0, stream, p);
-        else if (need <= 8)
-            hipLaunchKernelGGL((merge_kernel<64, __bf16, 8>), grid, dim3(256), 0, stream, p);
-        else
-            hipLaunchKernelGGL((merge_kernel<64, __bf16, 16>), grid, dim3(256), 0, stream, p);
-    } else {
-        if (need <= 4)
-            hipLaunchKernelGGL((merge_kernel<128, __bf16, 4>), grid, dim3(256), 0, stream, p);
-        else if (need <= 8)
-            hipLaunchKernelGGL((merge_kernel<128, __bf16, 8>), grid, dim3(256), 0, stream, p);
-        else
-            hipLaunchKernelGGL((merge_kernel<128, __bf16, 16>), grid, dim3(256), 0, stream, p);
-    }
+    const int need = min((p.nsplit + spi - 1) / spi, 16);
+    if (p.D == 64)
+        launch_merge_batch<64>(p, need, grid, stream);
+    else
+        launch_merge_batch<128>(p, need, grid, stream);
     return hipGetLastError();
 }
 
