@@ -826,9 +826,13 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
             // constant, so no register is cleared per block
             const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             f32x16 s_acc[NT];
+            // With two tiles per wave both are computed whatever their mask
+            // (an inactive tile's scores are masked to -inf below, and its
+            // K rows are finite), so that the two MFMA chains share one basic
+            // block; a lone tile is skipped when no row sees it.
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                if (active[t]) {
+                if (NT > 1 || active[t]) {
                     const int r = ktile[t] * 32 + lr;
                     const char *krow = kst + r * LY::ROWB;
 #pragma unroll
@@ -839,6 +843,17 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
                 } else {
                     s_acc[t] = zero16;
                 }
+            }
+            if constexpr (NT > 1) {
+                // K reads kept four ahead of the MFMAs that use them
+                // (masks: 0x100 LDS read, 0x008 MFMA)
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int i = 0; i < 2 * NKC - 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             }
             if (masked) {
                 // lane value i of a tile is key tile*32 + (i/4)*8 + hh*4 + i%4
@@ -877,7 +892,10 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
             const float mu = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                if (!active[t])
+                // as for S: with two tiles an inactive one runs too (its
+                // probabilities are 0 and its V rows finite), keeping both
+                // tiles' exponentials and P V in one basic block
+                if (NT == 1 && !active[t])
                     continue;
                 bf16x8 pb[2];
 #pragma unroll
