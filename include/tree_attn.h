@@ -163,6 +163,11 @@ size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
  *               partial is a convex combination of V rows, so fp16 keeps it
  *               to 2^-11 relative as long as every |V| entry is below 65504,
  *               the fp16 range: a precondition of split calls.
+ * Finite inputs: K and V rows of every prefix key and tree node a request
+ *   holds must be finite.  Keys a row does not see are weighted by exact
+ *   zeros inside 32- or 64-key tiles, so a NaN or Inf in such a row can
+ *   still reach outputs (0 * Inf is NaN); storage past a request's keys
+ *   (page tails, unused pages) is never read.
  * Host sizes: max_tree >= every T_b (<= 256), max_prefix >= every
  *   prefix_len[b] (<= max_pages_per_seq * page_size).  They size the launch
  *   so no call ever reads device data on the host.
