@@ -3,20 +3,30 @@
 
 One *step* is the whole hot path of one decode step over one batch of
 synthetic inputs: the plan (parent array -> ancestor bitmask, depth, position
-ids) and the attention (its kernel and, when the prefix is split, the split-K
-merge), run as one ``tree_attn_plan_fwd`` call, which builds the plan inside
-the attention kernel.  The same step as two calls (``tree_attn_plan``, then
-``tree_attn_fwd``) is reported beside it as ``two_call``.  Inputs are resident in HBM
-before timing starts; the step is replayed from HIP graphs so that the
-microsecond-scale launches are not limited by the Python launch rate, and
-successive steps rotate over enough input replicas that the working set does
-not stay in the 256 MB Infinity Cache.
+ids), the paged prefix, the masked tree and the split-K merge, run as one
+``tree_attn_plan_fwd`` call, which builds the plan inside the attention
+kernel.  Inputs are resident in HBM before timing starts.  Steps are replayed
+from HIP graphs holding one step per input replica (a replica cycle; a step
+count short of a cycle replays a graph of the remaining steps, captured
+beforehand), and successive steps rotate over enough replicas that the
+working set does not stay in the 256 MB Infinity Cache.  Before any timing,
+at least 150 ms of untimed steps bring the clocks up, whatever ``--warmup``
+says; then ``--warmup`` untimed steps, then exactly ``--steps`` steps timed
+with HIP events on the replay stream.  ``value`` is tree tokens per second of
+that GPU time.
+
+Beside it: ``fwd_only`` (tree_attn_fwd alone, mask words from an earlier
+plan), ``plan_only`` (tree_attn_plan alone), ``two_call`` (plan, then
+forward), and the attention kernel's own mean launch time, from which
+``roofline`` is computed.
 
 Default workload: ``chain16`` (budget 16: 1 request, prefix 2048, a 16-node
-chain, 32/8 heads, head_dim 128, bf16), the HBM-bound case.  The same run also
-measures ``moe`` (budget 256: 32 requests, prefix 4096, best-first trees of
-256 nodes, 32/4 heads), the MFMA-bound case, and reports it under
-``budget256``.  One JSON line goes to stdout; diagnostics go to stderr.
+chain, 32/8 heads, head_dim 128, bf16), the HBM-bound case.  The same run
+also measures ``moe`` (budget 256: 32 requests, prefix 4096, best-first trees
+of 256 nodes, 32/4 heads; under ``budget256``), ``tree256`` (one request of
+budget 256) and ``mixed`` (8 requests, prefixes 512..8192, budget 64), each
+with its roofline and CPU oracle baseline.  One JSON line goes to stdout;
+diagnostics go to stderr.
 """
 from __future__ import annotations
 
@@ -146,6 +156,11 @@ class Replica:
         self.call.partial()
         self.call.merge()
 
+    def plan(self):
+        """The plan alone (tree_attn_plan), reported separately."""
+        ta.plan(self.w.parent, self.w.tree_off, self.w.prefix_len, max_tree=self.max_tree,
+                out=self.plan_out)
+
 
 def replica_bytes(w: W.Workload) -> int:
     t = 0
@@ -164,8 +179,11 @@ def capture(fn, n_rep):
 
 class Runner:
     """Graphs over the replicas: ``chunk`` runs one step on every replica in
-    turn, ``single[r]`` one step on replica r, ``partial_chunk`` only the
-    attention kernel on every replica (for the per-launch kernel time)."""
+    turn (one replica cycle), ``partial_chunk`` only the attention kernel on
+    every replica (for the per-launch kernel time).  A step count that is not
+    a whole number of cycles replays a graph of the remaining steps, captured
+    beforehand by :meth:`prepare`, so that no capture and no per-step host
+    launch falls inside a timed region."""
 
     def __init__(self, reps, compare=True):
         self.reps = reps
@@ -177,30 +195,72 @@ class Runner:
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         self.chunk = capture(lambda: [r.step() for r in reps], 1)
-        self.single = [capture(r.step, 1) for r in reps]
+        self.rest = {}
         self.partial_chunk = capture(lambda: [r.partial() for r in reps], 1)
         # the comparison forms launch the same attention kernel symbol; a
         # profiling run can leave them out so that its trace holds the step's
         # launches only
         self.fwd_chunk = capture(lambda: [r.fwd() for r in reps], 1) if compare else None
         self.two_call_chunk = capture(lambda: [r.step_two_call() for r in reps], 1) if compare else None
+        self.plan_chunk = capture(lambda: [r.plan() for r in reps], 1) if compare else None
+        torch.cuda.synchronize()
+
+    def prepare(self, *counts):
+        """Capture the remainder graphs that ``run_steps`` needs for these
+        step counts (steps on replicas 0 .. k % R - 1)."""
+        R = len(self.reps)
+        for k in counts:
+            m = k % R
+            if m and m not in self.rest:
+                self.rest[m] = capture(lambda: [r.step() for r in self.reps[:m]], 1)
         torch.cuda.synchronize()
 
     def run_steps(self, k):
         R = len(self.reps)
         for _ in range(k // R):
             self.chunk.replay()
-        for i in range(k % R):
-            self.single[i].replay()
+        if k % R:
+            self.rest[k % R].replay()
 
 
-def time_steps(runner: Runner, steps: int, warmup: int) -> float:
+def ramp_clocks(runner: Runner, seconds: float = 0.15) -> float:
+    """Untimed GPU work before any timing (whatever --warmup says): whole
+    replica cycles until at least ``seconds`` of GPU time have passed, so
+    that the timed steps do not catch the clocks ramping up.  Returns the
+    GPU seconds spent."""
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    spent = 0.0
+    n = 1
+    while spent < seconds:
+        e0.record(stream)
+        for _ in range(n):
+            runner.chunk.replay()
+        e1.record(stream)
+        e1.synchronize()
+        spent += e0.elapsed_time(e1) / 1e3
+        n = min(n * 2, 64)
+    return spent
+
+
+def time_steps(runner: Runner, steps: int, warmup: int) -> tuple:
+    """``warmup`` untimed steps, then exactly ``steps`` steps bracketed by
+    device synchronisations.  Returns (GPU seconds from HIP events recorded
+    on the replay stream around the steps, host wall seconds)."""
+    runner.prepare(steps, warmup)
     runner.run_steps(warmup)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
     runner.run_steps(steps)
+    e1.record(stream)
     torch.cuda.synchronize()
-    return time.perf_counter() - t0
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / 1e3, wall
 
 
 def time_partial_kernel(runner: Runner, min_launches: int = 200, graph=None) -> float:
@@ -288,8 +348,30 @@ def traffic_for(workload: str):
 
 # ---------------------------------------------------------------- main
 
+def roofline(kind: str, wk: dict, t_kern: float, name: str, kernel: str, peak_flops: float) -> dict:
+    """Roofline entry of the step's attention kernel: algorithmic FLOPs
+    (``mfma``) or bytes (``hbm``) of one launch over its mean launch time."""
+    if kind == "mfma":
+        ach = wk["flops"] / t_kern / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": peak_flops, "unit": "TFLOP/s",
+                "frac": ach / peak_flops, "traffic": traffic_for(name), "kernel": kernel,
+                "kernel_us": t_kern * 1e6, "flops_per_launch": wk["flops"]}
+    ach = wk["kernel_bytes"] / t_kern / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": ach / PEAK_HBM_GBS, "traffic": traffic_for(name), "kernel": kernel,
+            "kernel_us": t_kern * 1e6, "bytes_per_launch": wk["kernel_bytes"]}
+
+
+# which roofline bounds each workload's attention kernel (mixed sits near the
+# ridge point, so both fractions are reported for it)
+BOUND = {"tiny": "hbm", "chain16": "hbm", "tree256": "mfma", "mixed": "mfma", "moe": "mfma"}
+
+
 def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: float,
             compare: bool = True) -> dict:
+    """One workload: ``warmup`` untimed steps after a clock ramp, then
+    exactly ``steps`` steps timed with HIP events on the replay stream.
+    ``value`` = tree tokens per second of GPU time over those steps."""
     w = W.make_config(name)
     per = replica_bytes(w)
     R = max(1, min(MAX_REPLICAS, math.ceil(ROTATE_BYTES / per)))
@@ -300,28 +382,34 @@ def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: flo
     runner = Runner(reps, compare)
     nsplit = reps[0].call.num_splits
     wk = work(w, nsplit)
-    dt = time_steps(runner, steps, warmup)
-    ms = dt / steps * 1e3
+    ramp = ramp_clocks(runner)
+    gpu_s, wall_s = time_steps(runner, steps, warmup)
+    ms = gpu_s / steps * 1e3
     t_kern = time_partial_kernel(runner)
     t_fwd = time_partial_kernel(runner, graph=runner.fwd_chunk) if compare else float("nan")
     t_two = time_partial_kernel(runner, graph=runner.two_call_chunk) if compare else float("nan")
-    log(f"[bench] {name}: {ms * 1e3:.2f} us/step (one call: plan inside the attention kernel), "
-        f"attention kernel {t_kern * 1e6:.2f} us/launch; plan then forward as two calls "
-        f"{t_two * 1e6:.2f} us, forward call alone (attention + merge) {t_fwd * 1e6:.2f} us, "
-        f"splits={nsplit}")
+    t_plan = time_partial_kernel(runner, graph=runner.plan_chunk) if compare else float("nan")
+    log(f"[bench] {name}: {ms * 1e3:.2f} us/step of GPU time ({wall_s / steps * 1e6:.2f} us wall; "
+        f"one call, the plan inside the attention kernel; {ramp * 1e3:.0f} ms clock ramp), "
+        f"attention kernel {t_kern * 1e6:.2f} us/launch; forward call alone {t_fwd * 1e6:.2f} us, "
+        f"plan alone {t_plan * 1e6:.2f} us, plan then forward {t_two * 1e6:.2f} us, splits={nsplit}")
     res = {
         "workload": name,
-        "value": wk["tree_tokens"] * steps / dt,
+        "value": wk["tree_tokens"] * steps / gpu_s,
         "ms_per_step": ms,
+        "wall_ms_per_step": wall_s / steps * 1e3,
+        "steps": steps,
+        "warmup": warmup,
         "num_splits": nsplit,
-        "tflops_step": wk["flops"] / (ms * 1e-3) / 1e12,
+        "tflops": wk["flops"] / (ms * 1e-3) / 1e12,
         "kernel_us": t_kern * 1e6,
-        # tree tokens per second of the forward call alone (attention kernel
-        # and split merge, the plan excluded), replayed back to back
+        # tree_attn_fwd alone (mask words from an earlier plan; attention
+        # kernel and split merge), replayed back to back: tree tokens per
+        # second over the forward call's GPU time, the plan excluded
         "fwd_only": ({"value": wk["tree_tokens"] / t_fwd, "unit": "tree tokens/s", "us": t_fwd * 1e6}
                      if compare else None),
-        # the same step as two calls (tree_attn_plan, then tree_attn_fwd),
-        # replayed back to back
+        # tree_attn_plan alone, and the step as two calls (plan, then forward)
+        "plan_only": {"us": t_plan * 1e6} if compare else None,
         "two_call": ({"value": wk["tree_tokens"] / t_two, "unit": "tree tokens/s", "us": t_two * 1e6}
                      if compare else None),
         "work": wk,
@@ -331,18 +419,11 @@ def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: flo
                    "num_splits": nsplit, "replicas": R},
     }
     is_bf16 = w.dtype == torch.bfloat16
-    if name == "moe" or name == "tree256" or name == "mixed":
-        ach = wk["flops"] / t_kern / 1e12
-        peak = PEAK_BF16_TFLOPS if is_bf16 else PEAK_FP32_TFLOPS
-        res["roofline"] = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
-                           "frac": ach / peak, "traffic": traffic_for(name),
-                           "kernel": "fwd_bf16_kernel", "kernel_us": t_kern * 1e6}
-    else:
-        ach = wk["kernel_bytes"] / t_kern / 1e9
-        res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                           "frac": ach / PEAK_HBM_GBS, "traffic": traffic_for(name),
-                           "kernel": "fwd_bf16_kernel" if is_bf16 else "fwd_f32_kernel",
-                           "kernel_us": t_kern * 1e6}
+    kernel = "fwd_bf16_kernel" if is_bf16 else "fwd_f32_kernel"
+    peak = PEAK_BF16_TFLOPS if is_bf16 else PEAK_FP32_TFLOPS
+    res["roofline"] = roofline(BOUND[name], wk, t_kern, name, kernel, peak)
+    if name == "mixed":
+        res["roofline_hbm"] = roofline("hbm", wk, t_kern, name, kernel, peak)
     del runner, reps
     torch.cuda.empty_cache()
     if cpu:
@@ -536,6 +617,17 @@ def calibrate_copy(mib: int, reps: int):
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": reps}))
 
 
+SUB_KEYS = ("value", "unit", "ms_per_step", "wall_ms_per_step", "steps", "warmup", "tflops",
+            "num_splits", "config", "roofline", "roofline_hbm", "cpu_baseline", "fwd_only",
+            "plan_only", "two_call")
+
+
+def sub_line(res: dict) -> dict:
+    out = {"workload": res["workload"], "unit": "tree tokens/s"}
+    out.update({k: res[k] for k in SUB_KEYS if k in res})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -543,11 +635,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="chain16", choices=[n for n in W.CONFIG_NAMES])
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the budget-256 (moe) measurement")
+                    help="skip the other bf16 workloads (moe, tree256, mixed) and the adjacent steps")
+    ap.add_argument("--no-adjacent", action="store_true",
+                    help="skip the adjacent steps (tree construction, commit, depth-first relabelling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true",
-                    help="skip the two-call and forward-only timings (profiling runs)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+                    help="skip the two-call, plan-only and forward-only timings (profiling runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle time budget of the headline workload (the others get half)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain copy kernel of this many MiB (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
@@ -576,8 +671,8 @@ def main():
     ta.load_library()
     dev = torch.device("cuda:0")
     cpu = not args.no_cpu_baseline
-    main_res = measure(args.workload, args.steps, args.warmup, dev, cpu, args.cpu_seconds,
-                       not args.no_compare)
+    compare = not args.no_compare
+    main_res = measure(args.workload, args.steps, args.warmup, dev, cpu, args.cpu_seconds, compare)
     w_dtype = "f32" if args.workload == "tiny" else "bf16"
     line = {
         "metric": METRIC,
@@ -597,23 +692,22 @@ def main():
     }
     if "cpu_baseline" in main_res:
         line["cpu_baseline"] = main_res["cpu_baseline"]
-    line["tflops"] = main_res["tflops_step"]
-    line["fwd_only"] = main_res["fwd_only"]
-    line["two_call"] = main_res["two_call"]
-    if not args.no_secondary and args.workload != "moe":
-        # 200 warm-up steps (about 120 ms of GPU work): with a handful the
-        # timed steps still caught the clocks ramping up (~7 % slow)
-        sec = measure("moe", max(20, args.steps // 10), max(200, args.warmup), dev, cpu,
-                      args.cpu_seconds, not args.no_compare)
-        line["budget256"] = {"workload": "moe", "value": sec["value"], "unit": "tree tokens/s",
-                             "ms_per_step": sec["ms_per_step"], "steps": max(20, args.steps // 10),
-                             "warmup": max(200, args.warmup),
-                             "tflops": sec["tflops_step"], "config": sec["config"],
-                             "roofline": sec["roofline"], "fwd_only": sec["fwd_only"],
-                             "two_call": sec["two_call"]}
-        if "cpu_baseline" in sec:
-            line["budget256"]["cpu_baseline"] = sec["cpu_baseline"]
+    line["value_definition"] = ("tree tokens (N) per second of GPU time over the timed steps; a step is "
+                                "one tree_attn_plan_fwd call (plan, paged prefix, masked tree and split "
+                                "merge), timed with HIP events on the replay stream")
+    for k in ("wall_ms_per_step", "tflops", "kernel_us", "fwd_only", "plan_only", "two_call"):
+        line[k] = main_res[k]
     if not args.no_secondary:
+        # steps per workload: about the same GPU time as the headline's at
+        # the default --steps; at least 20
+        plan_steps = {"moe": max(20, args.steps // 10), "tree256": args.steps,
+                      "mixed": max(20, args.steps // 5)}
+        for name, key in (("moe", "budget256"), ("tree256", "tree256"), ("mixed", "mixed")):
+            if name == args.workload:
+                continue
+            sec = measure(name, plan_steps[name], args.warmup, dev, cpu, args.cpu_seconds / 2, compare)
+            line[key] = sub_line(sec)
+    if not args.no_secondary and not args.no_adjacent:
         line["adjacent"] = measure_adjacent(dev)
         line["adjacent"]["depth_first_relabel"] = measure_dfs(dev)
     print(json.dumps(line), flush=True)

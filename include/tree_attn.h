@@ -90,6 +90,12 @@ const char *tree_attn_status_str(int status);
 /*
  * tree_attn_plan -- the ancestor sets of every tree node.
  *
+ * Defined by: JetFlow technical summary, section 2 (core architecture), the
+ * tree-causal attention mask -- a node sees the prefix and its in-tree
+ * ancestors, never siblings or descendants -- and the branch factorisation
+ * in the same paragraph, which conditions a node's token on the path up to
+ * and including the node (so A(i) holds i itself).
+ *
  * For local node i of request b, A(i) = {i} U A(parent[i]) with A(-1) empty:
  * the node's root path, itself included (the set of tree keys the node sees,
  * per the mask definition above).
@@ -134,6 +140,12 @@ size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
 
 /*
  * tree_attn_fwd -- tree-causal attention of every (node, q-head) row.
+ *
+ * Defined by: JetFlow technical summary, section 2 (core architecture), the
+ * tree-causal attention mask (the keys a node sees), used both by the causal
+ * parallel draft head and by target-model tree verification; section 3
+ * (industrial integration) for the prefix held in a paged KV cache
+ * addressed through block tables, as in the pages' vLLM integration.
  *
  * Row (n, h), n = tree_off[b] + i, kv head c = h / (Hq / Hkv) (contiguous
  * GQA groups), sees

@@ -18,7 +18,7 @@ import torch
 import oracle
 import tree_masked_attention_plan_amd as ta
 from tree_masked_attention_plan_amd import workloads as W
-from tests.test_gpu_parity import CASES, assert_close, sample_rows, small
+from tests.test_gpu_parity import CASES, assert_close, small
 
 pytestmark = pytest.mark.gpu
 
@@ -67,19 +67,13 @@ def check_plan(plan, parent, tree_off, prefix_len, max_tree, what=""):
 
 
 @pytest.mark.parametrize("name", W.CONFIG_NAMES)
-def test_named_workload(dev, name):
-    w = W.make_config(name)
+def test_named_workload(dev, name, named_reference):
+    """Every (node, head) row of each named workload against the oracle, and
+    the plan bit-exact."""
+    w, o_ref, l_ref = named_reference(name)
     plan, out, lse = run(w, dev)
     check_plan(plan, w.parent, w.tree_off, w.prefix_len, w.max_tree, name)
-    if name in ("mixed", "moe"):
-        rows = sample_rows(w, 3000, 8)
-        o_ref, l_ref = oracle.tree_attn_workload(w, rows=rows)
-        assert torch.isfinite(out).all() and torch.isfinite(lse).all()
-        assert_close(w, out.reshape(-1, w.D)[rows], lse.reshape(-1)[rows], o_ref, l_ref,
-                     f"{name} ({len(rows)} sampled rows)", raw=True)
-    else:
-        o_ref, l_ref = oracle.tree_attn_workload(w)
-        assert_close(w, out, lse, o_ref, l_ref, name, raw=True)
+    assert_close(w, out, lse, o_ref, l_ref, f"{name} (all {w.N * w.Hq} rows)", raw=True)
 
 
 @pytest.mark.parametrize("idx", range(len(CASES)), ids=[c[0] for c in CASES])

@@ -93,6 +93,19 @@ def _stream(device: torch.device, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _keep_for(stream, *tensors) -> None:
+    """Tie tensors allocated on the current stream to ``stream`` as well when
+    the kernels run on another one: the caching allocator then does not hand
+    their memory to a later allocation until ``stream`` has passed this
+    point (the workspace in particular, whose only reference is dropped when
+    a one-shot call returns)."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None and t.numel() > 0 and stream != torch.cuda.current_stream(t.device):
+            t.record_stream(stream)
+
+
 def _dev_tensor(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -145,6 +158,7 @@ def plan(parent: torch.Tensor, tree_off: torch.Tensor, prefix_len: torch.Tensor,
                                        int(max_tree), _ptr(out.anc_mask), _ptr(out.depth),
                                        _ptr(out.pos_id), _ptr(out.status), _stream(dev, stream))
     _raise(rc, "tree_attn_plan")
+    _keep_for(stream, *out)
     return out
 
 
@@ -184,6 +198,7 @@ def plan_dfs(parent: torch.Tensor, tree_off: torch.Tensor, prefix_len: torch.Ten
         _ptr(res.inv_perm), _ptr(res.parent_new), _ptr(res.plan.anc_mask), _ptr(res.plan.depth),
         _ptr(res.plan.pos_id), _ptr(res.plan.status), _stream(dev, stream))
     _raise(rc, "tree_attn_plan_dfs")
+    _keep_for(stream, res.perm, res.inv_perm, res.parent_new, *res.plan)
     return res
 
 
@@ -202,6 +217,7 @@ def gather_rows(src: torch.Tensor, index: torch.Tensor, *, out: Optional[torch.T
                                               int(index.numel()), int(row_bytes),
                                               _stream(src.device, stream))
     _raise(rc, "tree_attn_gather_rows")
+    _keep_for(stream, out)
     return out
 
 
@@ -221,6 +237,7 @@ def build_tree(logp: torch.Tensor, T: int, *, stream=None) -> Tuple[torch.Tensor
     rc = load_library().tree_attn_build_tree(_ptr(logp), B, Dmax, K, int(T), _ptr(parent), _ptr(choice),
                                              _ptr(score), _stream(dev, stream))
     _raise(rc, "tree_attn_build_tree")
+    _keep_for(stream, parent, choice, score)
     return parent, choice, score
 
 
@@ -266,6 +283,7 @@ def commit(anc_mask: torch.Tensor, depth: torch.Tensor, tree_off: torch.Tensor,
         num_pages, block_table.shape[1], int(max_tree), TA_DTYPE[dt], _ptr(new_prefix_len),
         _ptr(status), _stream(dev, stream))
     _raise(rc, "tree_attn_commit")
+    _keep_for(stream, new_prefix_len, status)
     return new_prefix_len, status
 
 
@@ -316,6 +334,7 @@ class FwdCall:
     def _call(self, fn, name, stream):
         rc = fn(*self._args, _stream(self.out.device, stream))
         _raise(rc, name)
+        _keep_for(stream, self.workspace, self.out, self.lse)
         return self
 
     def run(self, stream=None):
@@ -442,20 +461,24 @@ class PlanFwdCall:
         self.num_splits = nsplit
         self._lib = load_library()
 
+    def _kept(self, stream):
+        _keep_for(stream, self.workspace, self.out, self.lse, *self.plan)
+        return self
+
     def run(self, stream=None):
         rc = self._lib.tree_attn_plan_fwd(*self._args, _stream(self.out.device, stream))
         _raise(rc, "tree_attn_plan_fwd")
-        return self
+        return self._kept(stream)
 
     def partial(self, stream=None):
         rc = self._lib.tree_attn_plan_fwd_partial(*self._args, _stream(self.out.device, stream))
         _raise(rc, "tree_attn_plan_fwd_partial")
-        return self
+        return self._kept(stream)
 
     def merge(self, stream=None):
         rc = self._lib.tree_attn_merge(*self._fwd_args, _stream(self.out.device, stream))
         _raise(rc, "tree_attn_merge")
-        return self
+        return self._kept(stream)
 
 
 def prepare_plan_fwd(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, k_cache: torch.Tensor,

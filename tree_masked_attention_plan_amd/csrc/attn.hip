@@ -1093,7 +1093,7 @@ __global__ __launch_bounds__(256) void merge_kernel(FwdParams p)
     constexpr int SPI = 64 / LPS;     // splits per wave-wide load
     // BATCH: loads in flight per lane, sized by the host to the split count
     // the few arguments used, loaded together (opaque copies, as load_args)
-    const _Float16 *ws_o = p.ws_o;
+    const _Float16 *ws_o = (const _Float16 *)p.ws_o;
     const float *ws_lse = p.ws_lse;
     void *out = p.out;
     float *lse_out = p.lse;

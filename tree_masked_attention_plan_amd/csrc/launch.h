@@ -56,7 +56,7 @@ struct FwdParams {
     const uint64_t *anc_mask;
     void *out;
     float *lse;
-    _Float16 *ws_o;  // [nsplit, N, Hq, D] normalised partial outputs (fp16)
+    uint16_t *ws_o;  // [nsplit, N, Hq, D] normalised partial outputs (fp16 bit patterns)
     float *ws_lse;   // [nsplit, N, Hq] partial log2-sum-exp (scaled scores)
     int32_t B, N, Hq, Hkv, G, D;
     int32_t num_pages, max_pages, page_shift, max_tree;

@@ -143,7 +143,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // so fp16 holds it to 2^-11 relative; the partial lse stays fp32.
 size_t ws_o_bytes(int32_t nsplit, int32_t N, int32_t Hq, int32_t D)
 {
-    return align256((size_t)nsplit * N * Hq * D * sizeof(_Float16));
+    return align256((size_t)nsplit * N * Hq * D * sizeof(uint16_t));
 }
 
 size_t ws_bytes(const Geometry &g, int32_t N, int32_t Hq, int32_t D)
@@ -467,7 +467,7 @@ ta_status_t run_fwd(const void *q, const void *k_tree, const void *v_tree, const
     p.ws_o = nullptr;
     p.ws_lse = nullptr;
     if (g.nsplit > 1) {
-        p.ws_o = (_Float16 *)workspace;
+        p.ws_o = (uint16_t *)workspace;
         p.ws_lse = (float *)((char *)workspace + ws_o_bytes(g.nsplit, N, Hq, D));
     }
     p.B = B;
