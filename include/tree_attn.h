@@ -168,13 +168,16 @@ size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
  *   anc_mask    [N, TREE_ATTN_MASK_WORDS] u64, as written by tree_attn_plan
  *   out         [N, Hq, D] dtype;  lse [N, Hq] f32
  *   workspace   tree_attn_workspace_bytes(...) bytes, 256-byte aligned, or
- *               NULL when that is 0; its contents are scratch between calls.
- *               With more than one split (bf16 only) it holds each split's
- *               normalised partial output in fp16 ([splits, N, Hq, D]) and its
- *               partial log-sum-exp in fp32 ([splits, N, Hq]).  A normalised
- *               partial is a convex combination of V rows, so fp16 keeps it
- *               to 2^-11 relative as long as every |V| entry is below 65504,
- *               the fp16 range: a precondition of split calls.
+ *               NULL when that is 0; its contents are scratch between calls,
+ *               and one call at a time may use it (calls that share one must
+ *               be ordered: the same stream, or events).  With more than one
+ *               split (bf16 only) it holds each split's normalised partial
+ *               output in fp16 ([splits, N, Hq, D]), each row scaled by a
+ *               power of two 2^-e so that its largest magnitude lies in
+ *               [2^14, 2^15) -- any finite bf16 V stays in range, and the
+ *               scaling changes no rounding -- and the pairs (partial
+ *               log-sum-exp, e) in fp32 ([splits, N, Hq, 2]).  The split
+ *               merge then runs as a second kernel on the stream.
  * Finite inputs: K and V rows of every prefix key and tree node a request
  *   holds must be finite.  Keys a row does not see are weighted by exact
  *   zeros inside 32- or 64-key tiles, so a NaN or Inf in such a row can
@@ -361,8 +364,8 @@ ta_status_t tree_attn_commit(const uint64_t *anc_mask, const int32_t *depth, con
  * tree_attn_merge on the same stream.
  *   tree_attn_fwd_partial  launches the attention kernel.  With one prefix
  *                          split it writes out / lse itself; otherwise each
- *                          split writes its normalised partial output and its
- *                          partial log-sum-exp into the workspace.
+ *                          split writes its scaled partial output and its
+ *                          (log-sum-exp, scale exponent) into the workspace.
  *   tree_attn_merge        combines the splits' partials into out / lse by
  *                          the log-sum-exp rule (split-K merge); a no-op
  *                          when there is one split.  It must follow the

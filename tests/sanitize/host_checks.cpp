@@ -80,9 +80,9 @@ int main()
                 if (dt == TA_DTYPE_BF16 && p.nsplit > 1) {
                     CHECK(need > 0);
                     const char *o0 = (const char *)p.ws_o;
-                    const char *l0 = (const char *)p.ws_lse;
+                    const char *l0 = (const char *)p.ws_ml;
                     CHECK(o0 >= ws && o0 + (size_t)p.nsplit * s.N * s.Hq * s.D * 2 <= l0);
-                    CHECK(l0 + (size_t)p.nsplit * s.N * s.Hq * 4 <= ws + need);
+                    CHECK(l0 + (size_t)p.nsplit * s.N * s.Hq * 8 <= ws + need);
                     CHECK(p.chunk > 0 && (int64_t)p.chunk * (p.nsplit - 1) >= s.maxpre);
                 }
                 CHECK(p.units > 0 && p.units_per_xcd * 8 >= p.units);

@@ -222,22 +222,26 @@ def test_large_and_jumping_scores(dev, dtype):
         assert_close(w, out, lse, o_ref, l_ref, f"rescale {dtype} splits={ns}")
 
 
-def test_large_values_through_fp16_partials(dev):
-    """Split calls keep each split's normalised partial output in fp16.  A
-    partial is a convex combination of V rows, so it stays within the fp16
-    range when every |V| does: V scaled by 2^13 (|V| up to about 4e4, exact
-    in bf16) still matches the oracle, compared in units of the scale."""
+@pytest.mark.parametrize("log2_scale", [13, 17, 60, -60])
+def test_large_values_through_fp16_partials(dev, log2_scale):
+    """Split calls keep each split's normalised partial output in fp16, each
+    row scaled by a power of two so that its largest magnitude is in [2^14,
+    2^15).  V scaled by 2^13 (|V| up to about 4e4), 2^17 (about 6e5, beyond
+    the fp16 range), 2^60 (about 1e19) and 2^-60 (below the smallest fp16
+    subnormal) -- all exact in bf16 -- must still match the oracle through
+    splits 5, 17 and 64, compared in units of the scale."""
     rng = W.rng_for(23, 0)
     w = small("large-v", [1500, 300], [W.chain(16), W.best_first_tree(40, rng)], seed=23)
-    scale = 2.0 ** 13
+    scale = 2.0 ** log2_scale
     w.v_cache = (w.v_cache.float() * scale).to(torch.bfloat16)    # sentinel NaN slots stay NaN
     w.v_tree = (w.v_tree.float() * scale).to(torch.bfloat16)
     vmax = max(torch.nan_to_num(w.v_cache.float()).abs().max().item(), w.v_tree.float().abs().max().item())
-    assert 2.0 ** 14 < vmax < 65504.0
+    assert 2.0 ** (log2_scale + 1) < vmax < 2.0 ** (log2_scale + 4)
     o_ref, l_ref = oracle.tree_attn_workload(w)
     for ns in (0, 5, 17, 64):
         out, lse = gpu_fwd(w, dev, num_splits=ns)
-        assert_close(w, out / scale, lse, np.asarray(o_ref) / scale, l_ref, f"large-v splits={ns}")
+        assert_close(w, out / scale, lse, np.asarray(o_ref) / scale, l_ref,
+                     f"V * 2^{log2_scale} splits={ns}")
 
 
 def test_softmax_scale_override(dev):

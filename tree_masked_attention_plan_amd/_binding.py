@@ -93,6 +93,14 @@ def _stream(device: torch.device, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _after_current(stream, device) -> None:
+    """A call enqueued on another stream than the current one first waits
+    for the current stream, on which its inputs were produced and its
+    buffers allocated."""
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        stream.wait_stream(torch.cuda.current_stream(device))
+
+
 def _keep_for(stream, *tensors) -> None:
     """Tie tensors allocated on the current stream to ``stream`` as well when
     the kernels run on another one: the caching allocator then does not hand
@@ -332,6 +340,7 @@ class FwdCall:
         self._lib = load_library()
 
     def _call(self, fn, name, stream):
+        _after_current(stream, self.out.device)
         rc = fn(*self._args, _stream(self.out.device, stream))
         _raise(rc, name)
         _keep_for(stream, self.workspace, self.out, self.lse)
@@ -466,16 +475,19 @@ class PlanFwdCall:
         return self
 
     def run(self, stream=None):
+        _after_current(stream, self.out.device)
         rc = self._lib.tree_attn_plan_fwd(*self._args, _stream(self.out.device, stream))
         _raise(rc, "tree_attn_plan_fwd")
         return self._kept(stream)
 
     def partial(self, stream=None):
+        _after_current(stream, self.out.device)
         rc = self._lib.tree_attn_plan_fwd_partial(*self._args, _stream(self.out.device, stream))
         _raise(rc, "tree_attn_plan_fwd_partial")
         return self._kept(stream)
 
     def merge(self, stream=None):
+        _after_current(stream, self.out.device)
         rc = self._lib.tree_attn_merge(*self._fwd_args, _stream(self.out.device, stream))
         _raise(rc, "tree_attn_merge")
         return self._kept(stream)

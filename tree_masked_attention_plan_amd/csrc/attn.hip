@@ -27,7 +27,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));   // split partial outputs
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -38,6 +40,9 @@ static constexpr float kLn2 = 0.69314718055994530942f;
 static constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt left at their max)
+#define TA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
 // ---------------------------------------------------------------------------
 // shared helpers for the forward kernels
@@ -66,7 +71,7 @@ __device__ __forceinline__ FwdParams load_args(const FwdParams &in)
     FwdParams a = in;
     asm volatile("" : "+s"(a.q), "+s"(a.k_tree), "+s"(a.v_tree), "+s"(a.k_cache), "+s"(a.v_cache),
                       "+s"(a.block_table), "+s"(a.prefix_len), "+s"(a.tree_off), "+s"(a.anc_mask),
-                      "+s"(a.out), "+s"(a.lse), "+s"(a.ws_o), "+s"(a.ws_lse));
+                      "+s"(a.out), "+s"(a.lse), "+s"(a.ws_o), "+s"(a.ws_ml));
     asm volatile("" : "+s"(a.B), "+s"(a.N), "+s"(a.Hq), "+s"(a.Hkv), "+s"(a.G), "+s"(a.D),
                       "+s"(a.num_pages), "+s"(a.max_pages), "+s"(a.page_shift), "+s"(a.max_tree),
                       "+s"(a.nsplit), "+s"(a.chunk), "+s"(a.n_rt), "+s"(a.units),
@@ -153,6 +158,158 @@ __device__ __forceinline__ int64_t tree_row(const FwdParams &p, int off, int T, 
 }
 
 // ---------------------------------------------------------------------------
+// Cross-lane reductions on the VALU (DPP and the gfx950 lane swaps) rather
+// than through LDS.  Each step combines a lane with its partner under an
+// xor pattern (1, 2 in a quad; the mirrored lane in a half row and in a row;
+// the lane 16 and 32 away), so every lane ends with the same value, bit for
+// bit: each step adds the same two operands in every lane.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float dpp_f(float v, int ctrl_id)
+{
+    switch (ctrl_id) {
+    case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    }
+}
+
+// v[l] op v[l ^ 16] and v[l] op v[l ^ 32] in every lane, with the operands in
+// the same order in both lanes of a pair (lower row / half first)
+template <typename Op>
+__device__ __forceinline__ float xor16(float v, Op op)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+template <typename Op>
+__device__ __forceinline__ float xor32(float v, Op op)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op)
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        v = op(v, dpp_f(v, k));
+    return xor32(xor16(v, op), op);
+}
+
+// ---------------------------------------------------------------------------
+// split-K merge of RB (node, q head) rows by one wave, row ids r0[r] = n * Hq
+// + h (rows with on[r] false are skipped):
+//   lse = log2 sum_s 2^{lse_s};  O = sum_s 2^{lse_s - lse} O_s
+// where O_s = 2^{e_s} P_s and P_s is the stored fp16 row.  A partial row is
+// D fp16 values, read 8 at a time (16 bytes) by D/8 lanes, so one wave-wide
+// load covers SPI = 512/D splits; the loads of all RB rows (up to BATCH per
+// row, enough for 8 * SPI splits) and their (lse, e) pairs are in flight
+// before any is used.  Every split slot holds a pair for every row (lse =
+// -inf for a split that saw no key of the row's request), and partial rows
+// of zero-weight splits may hold stale data: a select excludes them.  The
+// additions run in increasing split order in every lane and do not depend
+// on RB, so every caller of this function gets the same bits.
+// ---------------------------------------------------------------------------
+template <int D, int RB>
+__device__ __forceinline__ void merge_rows_rb(const FwdParams &p, const int64_t (&r0)[RB], const bool (&on)[RB],
+                                              int lane)
+{
+    constexpr int LPS = D / 8;       // lanes per partial row
+    constexpr int SPI = 64 / LPS;    // partial rows per wave-wide load
+    constexpr int BATCH = 8;         // loads per lane per row in flight
+    const int ns = p.nsplit;
+    const int64_t split_stride = (int64_t)p.N * p.Hq;   // rows between splits
+    const int grp = lane / LPS;
+    const int dcol = (lane % LPS) * 8;
+    auto load = [&](int r, int s) {
+        const uint16_t *src = p.ws_o + (r0[r] + (int64_t)min(s, ns - 1) * split_stride) * D + dcol;
+        return *(const __attribute__((address_space(1))) f16x8 *)src;
+    };
+    f16x8 v[RB][BATCH];
+    float ls[RB];
+    int ex[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        if (!on[r])
+            continue;
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i)
+            if (i * SPI < ns)
+                v[r][i] = load(r, i * SPI + grp);
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        ls[r] = -INFINITY;
+        ex[r] = 0;
+        if (on[r] && lane < ns) {
+            const f32x2 m = gmem((const f32x2 *)p.ws_ml)[lane * split_stride + r0[r]];
+            ls[r] = m[0];
+            ex[r] = (int)m[1];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    auto fmax_op = [](float a, float b) { return fmaxf(a, b); };
+    auto add_op = [](float a, float b) { return a + b; };
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        if (!on[r])
+            continue;
+        const float mx = wave_reduce(ls[r], fmax_op);
+        const float base = (mx == -INFINITY) ? 0.f : mx;
+        const float wgt = (lane < ns) ? fast_exp2(ls[r] - base) : 0.f;
+        const float tot = wave_reduce(wgt, add_op);
+        const float wo = __builtin_ldexpf(wgt, ex[r]);   // weight of the stored (scaled) row
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        auto add = [&](const f16x8 &x, int s) {
+            const float ws = __shfl(wo, s & 63);
+            if (s < ns && ws > 0.f) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[j] += ws * (float)x[j];
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i)
+            if (i * SPI < ns)
+                add(v[r][i], i * SPI + grp);
+        for (int s0 = BATCH * SPI; s0 < ns; s0 += BATCH * SPI) {
+            f16x8 w[BATCH];
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i)
+                if (s0 + i * SPI < ns)
+                    w[i] = load(r, s0 + i * SPI + grp);
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i)
+                if (s0 + i * SPI < ns)
+                    add(w[i], s0 + i * SPI + grp);
+        }
+        // the LPS-lane groups hold the same columns of different splits
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (LPS <= 8)
+                acc[j] += __shfl_xor(acc[j], 8);
+            acc[j] = xor16(acc[j], add_op);
+            acc[j] = xor32(acc[j], add_op);
+        }
+        if (grp == 0) {
+            const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+            u32x4 w4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const __bf16 e0 = (__bf16)(acc[2 * j] * inv);
+                const __bf16 e1 = (__bf16)(acc[2 * j + 1] * inv);
+                w4[j] = (uint32_t)__builtin_bit_cast(uint16_t, e0) | ((uint32_t)__builtin_bit_cast(uint16_t, e1) << 16);
+            }
+            *(__attribute__((address_space(1))) u32x4 *)(gmem((uint16_t *)p.out) + r0[r] * D + dcol) = w4;
+        }
+        if (lane == 0)
+            gmem(p.lse)[r0[r]] = tot > 0.f ? (base + __builtin_log2f(tot)) * kLn2 : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // bf16 forward: D = head dim, NW = waves per workgroup (32 query rows each)
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16): S^T = K Q^T with K as the A
@@ -229,8 +386,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
-// s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt left at their max)
-#define TA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
 // Workgroup shape: NR row tiles of 32 query rows, each computed by KS waves
 // that split the keys of a step between them (NW = NR * KS waves):
@@ -274,8 +429,10 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     char *const v_st0 = kv_lds + SBYTES;
     char *const k_st1 = kv_lds + 2 * SBYTES;
     char *const v_st1 = kv_lds + 3 * SBYTES;
-    // running (max, sum) of every slice's rows, for the final combine
+    // running (max, sum) of every slice's rows, for the final combine, and
+    // the largest magnitude of each slice's share of a partial row
     __shared__ float2 ml_x[KS > 1 ? NR * KS * 32 : 1];
+    __shared__ float am_x[KS > 1 ? NR * KS * 32 : 1];
     // the request's parents and first bad node, when the plan is built here
     __shared__ int32_t par_l[kMaxTree];
     __shared__ int32_t first_bad_l;
@@ -347,13 +504,8 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     const bool row_ok = my_row < rows;
     const int node = row_ok ? my_row / p.G : 0;
     const int qh = u.c * p.G + (row_ok ? my_row - node * p.G : 0);
-    if (!R.owns_tree && R.kend <= R.kstart) {
-        // an empty prefix split: its rows' partial lse is -inf, so the merge
-        // gives it zero weight without reading the request geometry
-        if (row_ok && hh == 0 && ks == 0)
-            gmem(p.ws_lse)[((int64_t)u.s * p.N + R.off + node) * p.Hq + qh] = -INFINITY;
-        return;   // uniform across the workgroup
-    }
+    // (an empty prefix split, past its request's prefix, runs no key block:
+    // its rows' partial lse is -inf, so the merge gives it zero weight)
     const int c = u.c;
     const int64_t head_off = (int64_t)c * D;
     const int64_t row_stride = (int64_t)p.Hkv * D;   // elements between key rows
@@ -1032,13 +1184,13 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
         l_tot = lsum;
         m_fin = base;
     }
-    if (!row_ok)
-        return;
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const float lse2 = l_tot > 0.f ? m_fin + __builtin_log2f(l_tot) : -INFINITY;
     const int64_t n = R.off + node;
     const bool lse_writer = hh == 0 && ks == 0;
     if (p.nsplit == 1) {
+        if (!row_ok)
+            return;
         const auto orow = gmem((uint16_t *)p.out + (n * p.Hq + qh) * D);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -1058,7 +1210,35 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
         }
         if (lse_writer)
             gmem(p.lse)[n * p.Hq + qh] = lse2 * kLn2;
-    } else {
+        return;
+    }
+    // A split's partial row: the normalised output scaled by 2^-e so that its
+    // largest magnitude lies in [2^14, 2^15), inside the fp16 range whatever
+    // the range of V, with e stored beside its lse.  Scaling by a power of
+    // two changes no rounding, so the stored value is the fp16 rounding of
+    // the exact normalised value, scaled.
+    float am = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+        if (!owns_dt(dt))
+            continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            am = fmaxf(am, __builtin_fabsf(acc_o[dt][i]));
+    }
+    am = fmaxf(am, __shfl_xor(am, 32));
+    if (KS > 1) {
+        // the row's other columns belong to the other key slices
+        if (hh == 0)
+            am_x[(rtw * KS + ks) * 32 + lr] = am;
+        __syncthreads();
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2)
+            am = fmaxf(am, am_x[(rtw * KS + s2) * 32 + lr]);
+    }
+    const float mo = am * inv;
+    const int ex = mo > 0.f ? __builtin_amdgcn_frexp_expf(mo) - 15 : 0;   // mo * 2^-ex in [2^14, 2^15)
+    if (row_ok) {
         const auto orow = gmem(p.ws_o + (((int64_t)u.s * p.N + n) * p.Hq + qh) * D);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -1066,112 +1246,31 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
                 continue;
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                const f16x4 v = {(_Float16)(acc_o[dt][i4 * 4 + 0] * inv), (_Float16)(acc_o[dt][i4 * 4 + 1] * inv),
-                                 (_Float16)(acc_o[dt][i4 * 4 + 2] * inv), (_Float16)(acc_o[dt][i4 * 4 + 3] * inv)};
+                f16x4 v;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    v[j] = (_Float16)__builtin_ldexpf(acc_o[dt][i4 * 4 + j] * inv, -ex);
                 *(__attribute__((address_space(1))) f16x4 *)(orow + dt * 32 + i4 * 8 + hh * 4) = v;
             }
         }
         if (lse_writer)
-            gmem(p.ws_lse)[((int64_t)u.s * p.N + n) * p.Hq + qh] = lse2;
+            gmem((f32x2 *)p.ws_ml)[((int64_t)u.s * p.N + n) * p.Hq + qh] = f32x2{lse2, (float)ex};
     }
 }
 
 // ---------------------------------------------------------------------------
-// split-K merge: one wave per (node, q head) row, over all N * Hq rows
-//   lse = log2 sum_s 2^{lse_s};  O = sum_s 2^{lse_s - lse} O_s
-// Every split slot holds an lse for every row (-inf for an empty prefix
-// split), so the merge needs no request geometry.  A split's partial row is D
-// fp16 values, read four at a time by D/4 lanes, so one wave-wide load covers
-// SPI = 256/D splits; the lse and all partial loads of a batch are issued
-// before any is used (one memory latency per BATCH * SPI splits).  Partial rows
-// of zero-weight splits may hold stale data and are excluded by a select.
+// split-K merge: one wave per (node, q head) row, over all N * Hq rows.
 // ---------------------------------------------------------------------------
-template <int D, typename OutT, int BATCH>
-__global__ __launch_bounds__(256) void merge_kernel(FwdParams p)
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(FwdParams p_arg)
 {
-    constexpr int LPS = D / 4;        // lanes per split row
-    constexpr int SPI = 64 / LPS;     // splits per wave-wide load
-    // BATCH: loads in flight per lane, sized by the host to the split count
-    // the few arguments used, loaded together (opaque copies, as load_args)
-    const _Float16 *ws_o = (const _Float16 *)p.ws_o;
-    const float *ws_lse = p.ws_lse;
-    void *out = p.out;
-    float *lse_out = p.lse;
-    int N = p.N, Hq = p.Hq, ns = p.nsplit;
-    asm volatile("" : "+s"(ws_o), "+s"(ws_lse), "+s"(out), "+s"(lse_out), "+s"(N), "+s"(Hq), "+s"(ns));
-    const int lane = threadIdx.x & 63;
+    const FwdParams p = load_args(p_arg);
     const int64_t r0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // n * Hq + qh
-    if (r0 >= (int64_t)N * Hq)
+    if (r0 >= (int64_t)p.N * p.Hq)
         return;
-    const int64_t split_stride = (int64_t)N * Hq;   // rows between splits
-    const int grp = lane / LPS;       // which split of a load this lane takes
-    const int dcol = (lane % LPS) * 4;
-    const _Float16 *src = ws_o + r0 * D + dcol;
-
-    // The whole first batch and the lse are in flight before anything waits:
-    // partial rows first, the lse last (vmcnt counts in issue order).  Loads
-    // are unconditional, of a clamped slot, so that no branch separates them;
-    // a slot past the end is dropped by the weighting below.
-    auto load = [&](int s) {
-        return *(const __attribute__((address_space(1))) f16x4 *)(src + min(s, ns - 1) * split_stride * D);
-    };
-    f16x4 v[BATCH];
-#pragma unroll
-    for (int i = 0; i < BATCH; ++i)
-        v[i] = load(i * SPI + grp);
-    float ls = -INFINITY;
-    if (lane < ns)
-        ls = gmem(ws_lse)[lane * split_stride + r0];
-    __builtin_amdgcn_sched_barrier(0);
-    float mx = ls;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        mx = fmaxf(mx, __shfl_xor(mx, o));
-    const float base = (mx == -INFINITY) ? 0.f : mx;
-    const float wgt = (lane < ns) ? fast_exp2(ls - base) : 0.f;
-    float tot = wgt;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        tot += __shfl_xor(tot, o);
-
-    float4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto add = [&](const f16x4 &x, int s) {
-        const float ws = __shfl(wgt, s & 63);
-        if (s < ns && ws > 0.f) {
-            acc.x += ws * (float)x[0];
-            acc.y += ws * (float)x[1];
-            acc.z += ws * (float)x[2];
-            acc.w += ws * (float)x[3];
-        }
-    };
-#pragma unroll
-    for (int i = 0; i < BATCH; ++i)
-        add(v[i], i * SPI + grp);
-    for (int s0 = BATCH * SPI; s0 < ns; s0 += BATCH * SPI) {
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i)
-            v[i] = load(s0 + i * SPI + grp);
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i)
-            add(v[i], s0 + i * SPI + grp);
-    }
-#pragma unroll
-    for (int o = LPS; o < 64; o <<= 1) {
-        acc.x += __shfl_xor(acc.x, o);
-        acc.y += __shfl_xor(acc.y, o);
-        acc.z += __shfl_xor(acc.z, o);
-        acc.w += __shfl_xor(acc.w, o);
-    }
-    if (grp == 0) {
-        const float inv = tot > 0.f ? 1.0f / tot : 0.f;
-        __attribute__((address_space(1))) OutT *dst = gmem((OutT *)out) + r0 * D + dcol;
-        dst[0] = (OutT)(acc.x * inv);
-        dst[1] = (OutT)(acc.y * inv);
-        dst[2] = (OutT)(acc.z * inv);
-        dst[3] = (OutT)(acc.w * inv);
-    }
-    if (lane == 0)
-        gmem(lse_out)[r0] = tot > 0.f ? (base + __builtin_log2f(tot)) * kLn2 : -INFINITY;
+    const int64_t r[1] = {r0};
+    const bool on[1] = {true};
+    merge_rows_rb<D, 1>(p, r, on, threadIdx.x & 63);
 }
 
 // ---------------------------------------------------------------------------
@@ -1318,49 +1417,15 @@ hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nr, int ks, hipStr
     return hipGetLastError();
 }
 
-template <int D, int BATCH>
-static void launch_merge_n(const FwdParams &p, dim3 grid, hipStream_t stream)
-{
-    hipLaunchKernelGGL((merge_kernel<D, __bf16, BATCH>), grid, dim3(256), 0, stream, p);
-}
-
-template <int D>
-static void launch_merge_batch(const FwdParams &p, int need, dim3 grid, hipStream_t stream)
-{
-    switch (need) {
-    case 1: launch_merge_n<D, 1>(p, grid, stream); break;
-    case 2: launch_merge_n<D, 2>(p, grid, stream); break;
-    case 3: launch_merge_n<D, 3>(p, grid, stream); break;
-    case 4: launch_merge_n<D, 4>(p, grid, stream); break;
-    case 5: launch_merge_n<D, 5>(p, grid, stream); break;
-    case 6: launch_merge_n<D, 6>(p, grid, stream); break;
-    case 7: launch_merge_n<D, 7>(p, grid, stream); break;
-    case 8: launch_merge_n<D, 8>(p, grid, stream); break;
-    case 9: launch_merge_n<D, 9>(p, grid, stream); break;
-    case 10: launch_merge_n<D, 10>(p, grid, stream); break;
-    case 11: launch_merge_n<D, 11>(p, grid, stream); break;
-    case 12: launch_merge_n<D, 12>(p, grid, stream); break;
-    case 13: launch_merge_n<D, 13>(p, grid, stream); break;
-    case 14: launch_merge_n<D, 14>(p, grid, stream); break;
-    case 15: launch_merge_n<D, 15>(p, grid, stream); break;
-    default: launch_merge_n<D, 16>(p, grid, stream); break;
-    }
-}
-
 hipError_t launch_merge(const FwdParams &p, hipStream_t stream)
 {
     if (p.nsplit == 1)
         return hipSuccess;
     const dim3 grid((unsigned)(((int64_t)p.N * p.Hq + 3) / 4));
-    // one batch of loads covers BATCH * (256 / D) splits: the smallest batch
-    // that covers the call's slots (at most 16; more slots take further
-    // batches), so that no lane loads clamped copies of the last slot
-    const int spi = 256 / p.D;
-    const int need = min((p.nsplit + spi - 1) / spi, 16);
     if (p.D == 64)
-        launch_merge_batch<64>(p, need, grid, stream);
+        hipLaunchKernelGGL((merge_kernel<64>), grid, dim3(256), 0, stream, p);
     else
-        launch_merge_batch<128>(p, need, grid, stream);
+        hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

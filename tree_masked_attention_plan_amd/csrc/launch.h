@@ -56,8 +56,11 @@ struct FwdParams {
     const uint64_t *anc_mask;
     void *out;
     float *lse;
-    uint16_t *ws_o;  // [nsplit, N, Hq, D] normalised partial outputs (fp16 bit patterns)
-    float *ws_lse;   // [nsplit, N, Hq] partial log2-sum-exp (scaled scores)
+    // split-K workspace (nsplit > 1):
+    uint16_t *ws_o;    // [nsplit, N, Hq, D] normalised partial outputs, each row
+                       // scaled by 2^-e into fp16 range (fp16 bit patterns)
+    float *ws_ml;      // [nsplit, N, Hq, 2] (partial log2-sum-exp of the scaled
+                       // scores, e) per partial row
     int32_t B, N, Hq, Hkv, G, D;
     int32_t num_pages, max_pages, page_shift, max_tree;
     int32_t nsplit, chunk;          // prefix split count and keys per split

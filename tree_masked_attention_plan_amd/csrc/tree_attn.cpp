@@ -139,18 +139,23 @@ Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tre
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// A split's partial output is normalised (a convex combination of V rows),
-// so fp16 holds it to 2^-11 relative; the partial lse stays fp32.
+// Split workspace layout (nsplit > 1): the partial outputs (fp16, each row
+// scaled by a power of two), then the (lse, exponent) pairs.
 size_t ws_o_bytes(int32_t nsplit, int32_t N, int32_t Hq, int32_t D)
 {
     return align256((size_t)nsplit * N * Hq * D * sizeof(uint16_t));
+}
+
+size_t ws_ml_bytes(int32_t nsplit, int32_t N, int32_t Hq)
+{
+    return align256((size_t)nsplit * N * Hq * 2 * sizeof(float));
 }
 
 size_t ws_bytes(const Geometry &g, int32_t N, int32_t Hq, int32_t D)
 {
     if (g.nsplit <= 1 || N == 0)
         return 0;
-    return ws_o_bytes(g.nsplit, N, Hq, D) + align256((size_t)g.nsplit * N * Hq * sizeof(float));
+    return ws_o_bytes(g.nsplit, N, Hq, D) + ws_ml_bytes(g.nsplit, N, Hq);
 }
 
 ta_status_t check_fwd(const void *q, const void *k_tree, const void *v_tree, const void *k_cache,
@@ -465,10 +470,10 @@ ta_status_t run_fwd(const void *q, const void *k_tree, const void *v_tree, const
     p.out = out;
     p.lse = lse;
     p.ws_o = nullptr;
-    p.ws_lse = nullptr;
+    p.ws_ml = nullptr;
     if (g.nsplit > 1) {
         p.ws_o = (uint16_t *)workspace;
-        p.ws_lse = (float *)((char *)workspace + ws_o_bytes(g.nsplit, N, Hq, D));
+        p.ws_ml = (float *)((char *)workspace + ws_o_bytes(g.nsplit, N, Hq, D));
     }
     p.B = B;
     p.N = N;
