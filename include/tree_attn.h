@@ -64,7 +64,9 @@ typedef enum {
     TA_ERR_BAD_SHAPE = 2,   /* inconsistent or out-of-range sizes            */
     TA_ERR_UNSUPPORTED = 3, /* valid but not implemented (dtype, head_dim..) */
     TA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required    */
-    TA_ERR_HIP = 5          /* a HIP launch failed                           */
+    TA_ERR_HIP = 5,         /* a HIP launch failed                           */
+    TA_ERR_SCRATCH_LIMIT = 6 /* tree_attn_fwd_noalloc: the call needs more
+                                split workspace than its fixed array holds */
 } ta_status_t;
 
 typedef enum {
@@ -412,6 +414,38 @@ ta_status_t tree_attn_plan_fwd_partial(const void *q, const void *k_tree, const 
                                        int32_t num_splits, uint64_t *anc_mask, int32_t *depth,
                                        int32_t *pos_id, int32_t *status, void *out, float *lse,
                                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * tree_attn_fwd_noalloc -- tree_attn_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.
+ *
+ * The same operation, arguments, checks and results as tree_attn_fwd (bit for
+ * bit), without the workspace arguments: the split workspace comes from a
+ * fixed device array of TREE_ATTN_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library, one per device, held until the process ends.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * call on a device looks up that device's array address.
+ * Limit: a call whose tree_attn_workspace_bytes(...) exceeds
+ *   TREE_ATTN_NOALLOC_SCRATCH_BYTES returns TA_ERR_SCRATCH_LIMIT before
+ *   anything is launched (budget 16, 64 and 256 trees of one to eight
+ *   requests over prefixes of up to 8192 tokens fit; batches large enough
+ *   to need no split use no workspace at all).
+ * Every call on a device shares that device's array: calls that overlap on
+ *   one device (different streams without ordering, or threads) race and
+ *   give undefined results; order them.  The array keeps the last call's
+ *   contents; no call depends on what an earlier call left there.
+ */
+#define TREE_ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+ta_status_t tree_attn_fwd_noalloc(const void *q, const void *k_tree, const void *v_tree,
+                                  const void *k_cache, const void *v_cache,
+                                  const int32_t *block_table, const int32_t *prefix_len,
+                                  const int32_t *tree_off, const uint64_t *anc_mask,
+                                  int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t page_size, int32_t num_pages,
+                                  int32_t max_pages_per_seq, int32_t max_tree,
+                                  int32_t max_prefix, float softmax_scale, ta_dtype_t dtype,
+                                  int32_t num_splits, void *out, float *lse, void *stream);
 
 /*
  * The host-side argument check of tree_attn_fwd, on its own: returns exactly

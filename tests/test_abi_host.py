@@ -18,7 +18,8 @@ from tree_masked_attention_plan_amd import build as ta_build
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tree_attn.h")
 
-TA_OK, TA_ERR_NULL_PTR, TA_ERR_BAD_SHAPE, TA_ERR_UNSUPPORTED, TA_ERR_WORKSPACE, TA_ERR_HIP = range(6)
+TA_OK, TA_ERR_NULL_PTR, TA_ERR_BAD_SHAPE, TA_ERR_UNSUPPORTED, TA_ERR_WORKSPACE, TA_ERR_HIP, \
+    TA_ERR_SCRATCH_LIMIT = range(7)
 BF16, FP32 = 0, 1
 
 
@@ -41,7 +42,7 @@ def test_header_declares_the_boundary():
                      "tree_attn_plan_fwd",
                      "tree_attn_workspace_bytes",
                      "tree_attn_num_splits", "tree_attn_fwd_check", "tree_attn_status_str",
-                     "tree_attn_abi_version"):
+                     "tree_attn_abi_version", "tree_attn_fwd_noalloc"):
         assert required in names
 
 
@@ -63,8 +64,8 @@ def test_header_compiles_as_plain_c(tmp_path):
 
 def test_version_and_strings(lib):
     assert ta.abi_version() == 1
-    for code in range(6):
-        assert lib.tree_attn_status_str(code)
+    for code in range(7):
+        assert lib.tree_attn_status_str(code) != b"unknown status"
     assert lib.tree_attn_status_str(99) == b"unknown status"
 
 
@@ -320,3 +321,34 @@ def test_gather_rows_argument_checks(lib):
     assert gather_call(lib, dst=0) == TA_ERR_NULL_PTR
     assert gather_call(lib, src=0) == TA_ERR_NULL_PTR
     assert gather_call(lib, src=FAKE + 2) == TA_ERR_UNSUPPORTED       # not 4-byte aligned
+
+
+def call_noalloc(lib, **over):
+    a = fwd_args(**over)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.tree_attn_fwd_noalloc(P(a["q"]), P(a["k_tree"]), P(a["v_tree"]), P(a["k_cache"]),
+                                     P(a["v_cache"]), P(a["block_table"]), P(a["prefix_len"]),
+                                     P(a["tree_off"]), P(a["anc_mask"]), a["B"], a["N"], a["Hq"], a["Hkv"],
+                                     a["D"], a["page_size"], a["num_pages"], a["max_pages"], a["max_tree"],
+                                     a["max_prefix"], a["scale"], a["dtype"], a["num_splits"], P(a["out"]),
+                                     P(a["lse"]), None)
+
+
+def test_noalloc_refuses_beyond_its_array_before_launching(lib):
+    """The no-allocation forward computes its workspace need on the host and
+    refuses a call that needs more than its fixed array, before any HIP call
+    (this runs without a GPU)."""
+    limit = ta.NOALLOC_SCRATCH_BYTES
+    big = dict(B=1, N=256, max_tree=256, num_splits=64)
+    assert ta.workspace_bytes(1, 256, 32, 8, 128, 256, 2048, num_splits=64) > limit
+    assert call_noalloc(lib, **big) == TA_ERR_SCRATCH_LIMIT
+    assert lib.tree_attn_status_str(TA_ERR_SCRATCH_LIMIT).startswith(b"the call needs more split workspace")
+    # host argument errors come first when the workspace fits (or is not needed)
+    assert call_noalloc(lib, D=96) == TA_ERR_UNSUPPORTED
+    assert call_noalloc(lib, B=0, N=0, q=None, out=None, lse=None) == TA_OK
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define TREE_ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ta.NOALLOC_SCRATCH_BYTES

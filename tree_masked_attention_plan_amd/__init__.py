@@ -16,13 +16,16 @@ binding's entry points raises.
            k_cache, v_cache, block_table)  -> new_prefix_len, status
     plan_dfs(parent, tree_off, prefix_len) -> perm, inv_perm, parent_new, plan
     gather_rows(src, index)              -> src[index]
+    fwd_noalloc(..., out=, lse=)         -> out, lse  (no allocation; fixed
+                                            per-device split workspace)
 """
-from ._binding import (MASK_WORDS, MAX_TREE, FwdCall, PlanDfsResult, PlanFwdCall, PlanResult,
-                       TreeAttnError, abi_version, build_tree, check_status, commit, fwd, gather_rows,
-                       library_path, load_library, num_splits, plan, plan_dfs, plan_fwd, prepare_fwd,
+from ._binding import (MASK_WORDS, MAX_TREE, NOALLOC_SCRATCH_BYTES, FwdCall, PlanDfsResult, PlanFwdCall, PlanResult,
+                       TreeAttnError, abi_version, build_tree, check_status, commit, fwd, fwd_noalloc,
+                       gather_rows, library_path, load_library, num_splits, plan, plan_dfs, plan_fwd, prepare_fwd,
                        prepare_plan_fwd, workspace_bytes)
 
-__all__ = ["MASK_WORDS", "MAX_TREE", "FwdCall", "PlanDfsResult", "PlanFwdCall", "PlanResult",
-           "TreeAttnError", "abi_version", "build_tree", "check_status", "commit", "fwd", "gather_rows",
+__all__ = ["MASK_WORDS", "MAX_TREE", "NOALLOC_SCRATCH_BYTES", "FwdCall", "PlanDfsResult", "PlanFwdCall", "PlanResult",
+           "TreeAttnError", "abi_version", "build_tree", "check_status", "commit", "fwd", "fwd_noalloc",
+           "gather_rows",
            "library_path", "load_library", "num_splits", "plan", "plan_dfs", "plan_fwd", "prepare_fwd",
            "prepare_plan_fwd", "workspace_bytes"]

@@ -14,6 +14,7 @@ _LIB_NAME = "libtree_attn.so"
 
 MASK_WORDS = 4
 MAX_TREE = 256
+NOALLOC_SCRATCH_BYTES = 32 << 20   # TREE_ATTN_NOALLOC_SCRATCH_BYTES
 TA_DTYPE = {torch.bfloat16: 0, torch.float32: 1}
 
 _lib = None
@@ -60,6 +61,8 @@ def load_library():
         getattr(lib, name).argtypes = fwd_args[:9] + fwd_args[9:22] + [P, P, P, P] + fwd_args[22:] + [P]
     lib.tree_attn_fwd_check.restype = ctypes.c_int
     lib.tree_attn_fwd_check.argtypes = fwd_args
+    lib.tree_attn_fwd_noalloc.restype = ctypes.c_int
+    lib.tree_attn_fwd_noalloc.argtypes = fwd_args[:24] + [P]
     lib.tree_attn_build_tree.restype = ctypes.c_int
     lib.tree_attn_build_tree.argtypes = [P, i32, i32, i32, i32, P, P, P, P]
     lib.tree_attn_plan_dfs.restype = ctypes.c_int
@@ -322,6 +325,9 @@ def workspace_bytes(B: int, N: int, Hq: int, Hkv: int, D: int, max_tree: int, ma
                                                         TA_DTYPE[dtype], num_splits))
 
 
+_NO_WORKSPACE = object()   # prepare_fwd: marshal without a workspace (the no-allocation entry)
+
+
 class FwdCall:
     """One forward call with its arguments marshalled once.
 
@@ -407,7 +413,10 @@ def prepare_fwd(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, k_c
             raise ValueError("lse must be [N,Hq]")
     lib = load_library()
     need = lib.tree_attn_workspace_bytes(B, N, Hq, Hkv, D, max_tree, max_prefix, TA_DTYPE[dt], num_splits)
-    if workspace is None and need > 0:
+    no_ws = workspace is _NO_WORKSPACE
+    if no_ws:
+        workspace = None
+    elif workspace is None and need > 0:
         workspace = torch.empty(need + 256, dtype=torch.uint8, device=dev)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
@@ -423,8 +432,9 @@ def prepare_fwd(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, k_c
             _ptr(prefix_len), _ptr(tree_off), _ptr(anc_mask), B, N, Hq, Hkv, D, page_size, num_pages,
             max_pages, int(max_tree), int(max_prefix), sc, TA_DTYPE[dt], int(num_splits), _ptr(out),
             _ptr(lse), ws_ptr, ws_bytes)
-    rc = lib.tree_attn_fwd_check(*args)
-    _raise(rc, "tree_attn_fwd")
+    if not no_ws:
+        rc = lib.tree_attn_fwd_check(*args)
+        _raise(rc, "tree_attn_fwd")
     nsplit = lib.tree_attn_num_splits(B, Hq, Hkv, D, int(max_tree), int(max_prefix), TA_DTYPE[dt]) \
         if num_splits == 0 else num_splits
     return FwdCall(args, out, lse, workspace, nsplit)
@@ -540,3 +550,23 @@ def plan_fwd(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, k_cach
                             max_tree=max_tree, max_prefix=max_prefix, scale=scale, num_splits=num_splits)
     call.run(stream)
     return call.plan, call.out, call.lse
+
+
+def fwd_noalloc(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, k_cache: torch.Tensor,
+                v_cache: torch.Tensor, block_table: torch.Tensor, prefix_len: torch.Tensor,
+                tree_off: torch.Tensor, anc_mask: torch.Tensor, *, out: torch.Tensor, lse: torch.Tensor,
+                max_tree: int, max_prefix: int, scale: Optional[float] = None, num_splits: int = 0,
+                stream=None):
+    """:func:`fwd` through tree_attn_fwd_noalloc: the split workspace comes
+    from the library's fixed per-device array, and nothing is allocated here
+    either (``out``, ``lse``, ``max_tree`` and ``max_prefix`` are the
+    caller's).  Raises TreeAttnError with TA_ERR_SCRATCH_LIMIT when the call
+    needs more than NOALLOC_SCRATCH_BYTES of workspace."""
+    call = prepare_fwd(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, tree_off, anc_mask,
+                       max_tree=max_tree, max_prefix=max_prefix, scale=scale, num_splits=num_splits,
+                       out=out, lse=lse, workspace=_NO_WORKSPACE)
+    a = call._args
+    _after_current(stream, out.device)
+    rc = load_library().tree_attn_fwd_noalloc(*a[:24], _stream(out.device, stream))
+    _raise(rc, "tree_attn_fwd_noalloc")
+    return out, lse

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtree_attn.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("attn.hip", "plan.hip", "tree.hip", "commit.hip", "tree_attn.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("attn.hip", "plan.hip", "tree.hip", "commit.hip", "noalloc.hip", "tree_attn.cpp")]
 ARCH = "gfx950"
 
 

@@ -220,6 +220,7 @@ const char *tree_attn_status_str(int status)
     case TA_ERR_UNSUPPORTED: return "unsupported configuration (dtype, head_dim, page_size or tree size)";
     case TA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case TA_ERR_HIP: return "HIP launch failed";
+    case TA_ERR_SCRATCH_LIMIT: return "the call needs more split workspace than the no-allocation entry point holds";
     default: return "unknown status";
     }
 }
