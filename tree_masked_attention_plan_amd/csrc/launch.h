@@ -103,7 +103,7 @@ constexpr int kTreeMaxLogp = 4096;     // Dmax * K
 hipError_t launch_plan(const PlanParams &p, hipStream_t stream);
 hipError_t launch_plan_dfs(const PlanDfsParams &p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams &p, hipStream_t stream);
-// best-first draft trees: one wave per request
+// best-first draft trees: one workgroup per request
 hipError_t launch_build_tree(const TreeParams &p, hipStream_t stream);
 // accepted-path commit: one workgroup per request
 hipError_t launch_commit(const CommitParams &p, hipStream_t stream);

@@ -9,25 +9,36 @@
 namespace ta {
 
 // ---------------------------------------------------------------------------
-// best-first draft trees: one wave per request.
+// best-first draft trees, data-parallel: one 256-thread workgroup per request.
 //
-// Equal scores go to the earlier push.  In the sequential definition the
-// root's children are pushes 0..K-1 and node i's children K + K*i .. +K-1,
-// i.e. pushes are ordered by (parent + 1, token): that pair, with the
-// candidate's depth appended, is the tie-break tag (cand_tag).
+// The sequential definition pops candidates in the order (score desc, push
+// number asc); the root's children are pushes 0..K-1 and node i's children
+// K + K*i .. +K-1, so push numbers are ordered by (parent's pop index + 1,
+// token).  Node i's pop index is its position in that same order, so the
+// order of any two nodes is decided by their scores, then by the positions
+// of their parents in the order, then by their tokens -- and positions may
+// be taken in any subset that holds both parents: only the relative order of
+// nodes matters, and it never changes.
 //
-// Every child of a node is pushed when the node is popped, and the children
-// of one parent leave the pool in the pop order, (score desc, push number
-// asc).  So at any time only the best not-yet-popped child of each popped
-// node can be the next pop.  The pool holds just that one representative per
-// parent: a pop removes the winner w, adds w's next sibling in its parent's
-// order (the best sibling whose key is below w's) and w's own best child.
-// The pop sequence, and with it every output, is that of the full
-// expansion, with at most T + 1 live candidates.  Scores are the same fp32
-// sums, in the same order, so every comparison is decided identically.
+// A child never precedes its parent (its score is the parent's plus a
+// log-probability <= 0, and on equal scores the parent's push number is the
+// smaller), so the T pops are the first T nodes of the whole implicit tree
+// in this order, and that set is closed under taking parents.  The kernel
+// builds it depth by depth: it keeps the best (at most T) nodes found so far,
+// sorted; at depth d it adds the children of the kept depth-d nodes and keeps
+// the best T again.  A node that drops out has T better nodes, and so do all
+// its descendants, so nothing dropped can come back; after the last depth
+// the kept list is exactly the pop sequence, and a node's id is its position
+// in it.
 //
-// The pool sits in registers, a few 64-bit keys per lane; a pop is a
-// per-lane max and one wave-wide max.
+// Each step places the new children by counting: a child's new position is
+// the number of kept nodes above it (a binary search in the sorted list)
+// plus the number of new children above it; a kept node moves down by the
+// number of new children above it.  Once the list holds T nodes, a child
+// below its last node is dropped before counting, so after the first levels
+// only a few children per depth are counted.  Scores are the same fp32 sums
+// as in the sequential definition (parent score + one log-probability), so
+// every comparison is decided identically.
 // ---------------------------------------------------------------------------
 // A candidate as one 64-bit key whose unsigned order is the pop order:
 // larger score first (the float's bits mapped to an order-preserving
@@ -57,44 +68,6 @@ __device__ __forceinline__ void cand_of_key(uint64_t k, float &s, int &e)
     e = (int)(0xFFFFFFFFu - (uint32_t)k);
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
-{
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)
-{
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// max of 64-bit keys inside each row of 16 lanes: every lane of a row gets
-// its row's max (DPP rotations)
-__device__ __forceinline__ uint64_t row_max_key(uint64_t k)
-{
-    uint64_t o;
-    o = dpp_u64<0x121>(k); k = o > k ? o : k;   // row_ror:1
-    o = dpp_u64<0x122>(k); k = o > k ? o : k;   // row_ror:2
-    o = dpp_u64<0x124>(k); k = o > k ? o : k;   // row_ror:4
-    o = dpp_u64<0x128>(k); k = o > k ? o : k;   // row_ror:8
-    return k;
-}
-
-// wave-wide max of 64-bit keys; every lane gets the result (the row maxima,
-// then the four of them through readlane)
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k)
-{
-    k = row_max_key(k);
-    const uint64_t r0 = readlane_u64(k, 0), r1 = readlane_u64(k, 16);
-    const uint64_t r2 = readlane_u64(k, 32), r3 = readlane_u64(k, 48);
-    const uint64_t a = r0 > r1 ? r0 : r1, c = r2 > r3 ? r2 : r3;
-    return a > c ? a : c;
-}
-
 // A candidate's tie-break tag: (parent + 1, k) in the order of the push
 // numbers (K + K*parent + k, root children k), which it replaces, with the
 // candidate's depth below them (tags are unique without it, so it never
@@ -104,116 +77,270 @@ __device__ __forceinline__ int cand_tag(int par, int k, int depth)
     return ((par + 1) << 14) | (k << 8) | depth;
 }
 
-__global__ __launch_bounds__(64) void build_tree_kernel(TreeParams p)
+// Inclusive prefix sum of one int per thread over a 256-thread workgroup.
+__device__ __forceinline__ int block_scan_incl(int v, int tid, int32_t *wsum)
 {
-    // pool positions: one per pop plus the root's first child
-    constexpr int NS = (kMaxTree + 1 + 63) / 64;
-    __shared__ float lps[kTreeMaxLogp];      // this request's log-probabilities
-    __shared__ float node_score[kMaxTree];
-    // outputs are staged here and written once at the end
-    __shared__ int32_t o_parent[kMaxTree], o_choice[kMaxTree];
-    const int b = blockIdx.x;
-    const int lane = threadIdx.x;
-    const int K = p.K, T = p.T, Dmax = p.Dmax;
-    const float kEmpty = __builtin_nanf("");
-    const float *lp = p.logp + (int64_t)b * Dmax * K;
-    for (int i = lane; i < Dmax * K; i += 64)
-        lps[i] = lp[i];
-    for (int i = lane; i < T; i += 64) {
-        o_parent[i] = -1;
-        o_choice[i] = -1;
-        node_score[i] = kEmpty;
+    const int lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o);
+        v += lane >= o ? t : 0;
     }
+    if (lane == 63)
+        wsum[wv] = v;
     __syncthreads();
-    uint64_t slot[NS];
+    int add = 0;
 #pragma unroll
-    for (int q = 0; q < NS; ++q)
-        slot[q] = 0ull;
-    // the root's best child opens the pool (key 0: no candidate)
-    const uint64_t root_first = wave_max_key(lane < K ? cand_key(lps[lane], cand_tag(-1, lane, 1)) : 0ull);
-    if (lane == 0)
-        slot[0] = root_first;
-    int cnt = 1;   // pool positions used (uniform)
-    for (int i = 0; i < T; ++i) {
-        uint64_t lb = slot[0];
+    for (int w = 0; w < 3; ++w)
+        add += w < wv ? wsum[w] : 0;
+    __syncthreads();   // wsum is reused by the next scan
+    return v + add;
+}
+
+// The new position of each of m children (keys ckey) among the n kept nodes
+// (keys lkey, sorted best first) and the other children: the kept nodes above
+// it (binary search) plus the children above it (all keys are distinct).
+// Thread tid ranks children tid, tid + 256, ... (CPT of them, all at once),
+// so every child key read from LDS serves all of them, and the reads of a
+// block of keys are in flight together.  hist[i] counts the children whose
+// binary-search position is i (< n).
+template <int CPT>
+__device__ __forceinline__ void rank_children(const uint64_t *ckey, int32_t *cpos, int32_t *hist,
+                                              const uint64_t *lkey, int n, int m, int tid)
+{
+    constexpr int NT = 256;
+    uint64_t kc[CPT];
+    int lo[CPT], hi[CPT], rc[CPT];
 #pragma unroll
-        for (int q = 1; q < NS; ++q)
-            lb = slot[q] > lb ? slot[q] : lb;
-        const uint64_t kw = wave_max_key(lb);
-        if (kw == 0ull)
-            break;   // no candidate left: only with NaN inputs (the host checks
-                     // that the implicit tree holds T nodes); the remaining
-                     // nodes keep parent -1, choice -1, score NaN
-        float ws;
-        int e;
-        cand_of_key(kw, ws, e);                   // uniform
-        const int par = (e >> 14) - 1;
-        const int k = (e >> 8) & 63;
-        const int depth = e & 255;
-        const int dp = depth - 1;
-        // a node's score was written by lane 0 of this wave in an earlier
-        // pop; the wave's LDS accesses complete in program order
-        const float sp = par < 0 ? 0.f : node_score[par];
-        if (lane == 0) {
-            o_parent[i] = par;
-            o_choice[i] = k;
-            node_score[i] = ws;
+    for (int t = 0; t < CPT; ++t) {
+        const int c = tid + t * NT;
+        kc[t] = c < m ? ckey[c] : ~0ull;   // past the children: above every key
+        lo[t] = 0;
+        hi[t] = n;
+        rc[t] = 0;
+    }
+    // binary searches, interleaved (at most 9 rounds for n <= 256)
+    for (int round = 0; round < 9; ++round) {
+#pragma unroll
+        for (int t = 0; t < CPT; ++t) {
+            if (lo[t] < hi[t]) {
+                const int mid = (lo[t] + hi[t]) >> 1;
+                if (lkey[mid] > kc[t])
+                    lo[t] = mid + 1;
+                else
+                    hi[t] = mid;
+            }
         }
-        // w's next sibling: the best child of its parent whose key is below
-        // w's; and node i's best child, when it is below the depth limit.
-        // With K <= 16 the two searches share one pass: sibling candidates
-        // in lanes 0..15, child candidates in lanes 16..31.
-        uint64_t k_sib, k_child;
-        if (K <= 16) {
-            // one LDS read for both searches: lanes 0..15 read the parent's
-            // row of log-probabilities, lanes 16..31 node i's
-            const int j = lane & 15;
-            const bool sib = lane < 16;
-            const int row = sib ? dp : depth;
-            const bool live = lane < 32 && j < K && (sib || depth < Dmax);
-            const float v = live ? lps[row * K + j] : 0.f;
-            uint64_t key = 0ull;
-            if (live) {
-                if (sib) {
-                    const uint64_t c = cand_key(par < 0 ? v : sp + v, cand_tag(par, j, depth));
-                    key = c < kw ? c : 0ull;
-                } else {
-                    key = cand_key(ws + v, cand_tag(i, j, depth + 1));
+    }
+    constexpr int U = 8;   // child keys per block of reads
+    int c2 = 0;
+    for (; c2 + U <= m; c2 += U) {
+        uint64_t x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            x[u] = ckey[c2 + u];
+#pragma unroll
+        for (int t = 0; t < CPT; ++t)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                rc[t] += x[u] > kc[t] ? 1 : 0;
+    }
+    for (; c2 < m; ++c2) {
+        const uint64_t x = ckey[c2];
+#pragma unroll
+        for (int t = 0; t < CPT; ++t)
+            rc[t] += x > kc[t] ? 1 : 0;
+    }
+#pragma unroll
+    for (int t = 0; t < CPT; ++t) {
+        const int c = tid + t * NT;
+        if (c < m) {
+            cpos[c] = lo[t] + rc[t];
+            if (lo[t] < n)
+                atomicAdd(&hist[lo[t]], 1);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void build_tree_kernel(TreeParams p)
+{
+    constexpr int NT = 256;
+    constexpr int CH = 2048;   // children counted per step
+    __shared__ float lps[kTreeMaxLogp];   // this request's log-probabilities
+    // the kept nodes, best first, double-buffered: order key, score,
+    // parent position (-1: hangs off the prefix), token << 8 | depth
+    __shared__ uint64_t lkey[2][kMaxTree];
+    __shared__ float lsc[2][kMaxTree];
+    __shared__ int32_t lpar[2][kMaxTree];
+    __shared__ int32_t lkd[2][kMaxTree];
+    // the children of one step
+    __shared__ uint64_t ckey[CH];
+    __shared__ float csc[CH];
+    __shared__ int32_t cinfo[CH];   // (parent position + 1) << 8 | token
+    __shared__ int32_t cpos[CH];
+    // the kept depth-d nodes at the start of depth d: score, and where each
+    // is now (-1 once dropped)
+    __shared__ float par_sc[kMaxTree];
+    __shared__ int32_t par_at[kMaxTree];
+    __shared__ int32_t newpos[kMaxTree];
+    __shared__ int32_t hist[kMaxTree];
+    __shared__ int32_t wsum[4];
+    __shared__ int32_t s_count, s_grew;
+
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int K = p.K, T = p.T, Dmax = p.Dmax;
+    const float *lp = p.logp + (int64_t)b * Dmax * K;
+    for (int i = tid; i < Dmax * K; i += NT)
+        lps[i] = lp[i];
+    __syncthreads();
+
+    int n = 0;     // kept nodes (uniform)
+    int buf = 0;   // which list buffer is current (uniform)
+    for (int d = 0; d < Dmax; ++d) {
+        // the kept depth-d nodes (for d = 0 the virtual root), compacted
+        __syncthreads();   // every thread has read the previous depth's flags
+        if (tid == 0) {
+            s_count = 0;
+            s_grew = 0;
+        }
+        __syncthreads();
+        int nd = 1;
+        if (d > 0) {
+            for (int i0 = 0; i0 < n; i0 += NT) {
+                const int i = i0 + tid;
+                const bool at_d = i < n && (lkd[buf][i] & 255) == d;
+                const uint64_t bal = __ballot(at_d);
+                int wbase = 0;
+                if (lane == 0 && bal != 0ull)
+                    wbase = atomicAdd(&s_count, __builtin_popcountll(bal));
+                wbase = __shfl(wbase, 0);
+                if (at_d) {
+                    const int idx = wbase + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+                    par_sc[idx] = lsc[buf][i];
+                    par_at[idx] = i;
                 }
             }
-            key = row_max_key(key);
-            k_sib = readlane_u64(key, 0);
-            k_child = readlane_u64(key, 16);
-        } else {
-            uint64_t ks = 0ull;
-            if (lane < K) {
-                const float v = lps[dp * K + lane];
-                const uint64_t c = cand_key(par < 0 ? v : sp + v, cand_tag(par, lane, depth));
-                ks = c < kw ? c : 0ull;
+            __syncthreads();
+            nd = s_count;
+        }
+        const int npairs = nd * K;
+        for (int base = 0; base < npairs; base += CH) {
+            const int cnt = min(CH, npairs - base);
+            __syncthreads();
+            if (tid == 0)
+                s_count = 0;
+            __syncthreads();
+            const bool full = n == T;
+            const uint64_t thr = full ? lkey[buf][T - 1] : 0ull;
+            for (int j0 = 0; j0 < cnt; j0 += NT) {
+                const int j = j0 + tid;
+                bool v = false;
+                uint64_t key = 0ull;
+                float sc = 0.f;
+                int info = 0;
+                if (j < cnt) {
+                    const int pr = base + j;
+                    const int pi = pr / K;            // which parent
+                    const int k = pr - pi * K;        // which token
+                    const int ppos = d == 0 ? -1 : par_at[pi];
+                    if (d == 0 || ppos >= 0) {
+                        const float lv = lps[d * K + k];
+                        sc = d == 0 ? lv : par_sc[pi] + lv;
+                        if (sc == sc) {   // NaN candidates are never chosen
+                            key = cand_key(sc, cand_tag(ppos, k, d + 1));
+                            v = !full || key > thr;
+                            info = ((ppos + 1) << 8) | k;
+                        }
+                    }
+                }
+                const uint64_t bal = __ballot(v);
+                int wbase = 0;
+                if (lane == 0 && bal != 0ull)
+                    wbase = atomicAdd(&s_count, __builtin_popcountll(bal));
+                wbase = __shfl(wbase, 0);
+                if (v) {
+                    const int idx = wbase + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+                    ckey[idx] = key;
+                    csc[idx] = sc;
+                    cinfo[idx] = info;
+                }
             }
-            uint64_t kc = 0ull;
-            if (depth < Dmax && lane < K)
-                kc = cand_key(ws + lps[depth * K + lane], cand_tag(i, lane, depth + 1));
-            k_sib = wave_max_key(ks);
-            k_child = wave_max_key(kc);
+            if (tid < n)
+                hist[tid] = 0;
+            __syncthreads();
+            const int m = s_count;
+            if (m == 0)
+                continue;   // uniform
+            // new positions: kept nodes above a child (binary search in the
+            // sorted list) plus new children above it
+            const int cpt = (m + NT - 1) / NT;   // children per thread (uniform)
+            if (cpt == 1)
+                rank_children<1>(ckey, cpos, hist, lkey[buf], n, m, tid);
+            else if (cpt == 2)
+                rank_children<2>(ckey, cpos, hist, lkey[buf], n, m, tid);
+            else if (cpt <= 4)
+                rank_children<4>(ckey, cpos, hist, lkey[buf], n, m, tid);
+            else
+                rank_children<CH / NT>(ckey, cpos, hist, lkey[buf], n, m, tid);
+            __syncthreads();
+            // a kept node at position i moves down by the children above it,
+            // those whose binary-search position is <= i
+            const int cum = block_scan_incl(tid < n ? hist[tid] : 0, tid, wsum);
+            if (tid < n) {
+                const int np = tid + cum;
+                newpos[tid] = np < T ? np : -1;
+            }
+            __syncthreads();
+            const int nb = buf ^ 1;
+            if (tid < n && newpos[tid] >= 0) {
+                const int np = newpos[tid];
+                const int par = lpar[buf][tid];
+                // a kept node's parent precedes it, so it is kept too
+                const int par2 = par < 0 ? -1 : newpos[par];
+                const int kd = lkd[buf][tid];
+                const float sc = lsc[buf][tid];
+                lpar[nb][np] = par2;
+                lkd[nb][np] = kd;
+                lsc[nb][np] = sc;
+                lkey[nb][np] = cand_key(sc, cand_tag(par2, kd >> 8, kd & 255));
+            }
+            for (int c = tid; c < m; c += NT) {
+                const int np = cpos[c];
+                if (np < T) {
+                    const int info = cinfo[c];
+                    const int ppos = (info >> 8) - 1;
+                    const int k = info & 255;
+                    const int par2 = ppos < 0 ? -1 : newpos[ppos];
+                    lpar[nb][np] = par2;
+                    lkd[nb][np] = (k << 8) | (d + 1);
+                    lsc[nb][np] = csc[c];
+                    lkey[nb][np] = cand_key(csc[c], cand_tag(par2, k, d + 1));
+                    s_grew = 1;
+                }
+            }
+            // where this depth's parents are now
+            for (int i = tid; i < nd && d > 0; i += NT) {
+                const int q = par_at[i];
+                par_at[i] = q < 0 ? -1 : newpos[q];
+            }
+            n = min(n + m, T);
+            buf = nb;
         }
-        // the sibling takes the winner's place; the child takes a new position
-#pragma unroll
-        for (int q = 0; q < NS; ++q)
-            slot[q] = slot[q] == kw ? k_sib : slot[q];
-        if (k_child != 0ull) {
-            const int pos_lane = cnt & 63, pos_q = cnt >> 6;
-#pragma unroll
-            for (int q = 0; q < NS; ++q)
-                slot[q] = (q == pos_q && lane == pos_lane) ? k_child : slot[q];
-            ++cnt;
-        }
+        __syncthreads();
+        // no depth d + 1 node was kept: no deeper node can be either
+        if (!s_grew)
+            break;   // uniform
     }
-    __syncthreads();
-    for (int i = lane; i < T; i += 64) {
-        p.parent[(int64_t)b * T + i] = o_parent[i];
-        p.choice[(int64_t)b * T + i] = o_choice[i];
-        p.score[(int64_t)b * T + i] = node_score[i];
+    // node i is the i-th kept node; positions past the kept nodes are left
+    // without a candidate (only when NaN candidates leave fewer than T)
+    for (int i = tid; i < T; i += NT) {
+        const bool have = i < n;
+        const int kd = have ? lkd[buf][i] : 0;
+        p.parent[(int64_t)b * T + i] = have ? lpar[buf][i] : -1;
+        p.choice[(int64_t)b * T + i] = have ? (kd >> 8) : -1;
+        p.score[(int64_t)b * T + i] = have ? lsc[buf][i] : __builtin_nanf("");
     }
 }
 
@@ -224,7 +351,7 @@ hipError_t launch_build_tree(const TreeParams &p, hipStream_t stream)
 {
     if (p.B == 0 || p.T == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(build_tree_kernel, dim3(p.B), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(build_tree_kernel, dim3(p.B), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
