@@ -81,7 +81,10 @@ __device__ __forceinline__ FwdParams load_args(const FwdParams &in)
 
 // Workgroups are dealt round-robin to the 8 XCDs (id % 8).  Give each XCD a
 // contiguous run of work units so that the row tiles reading the same K/V
-// chunk run together on one XCD and share its L2.
+// chunk (consecutive ids) run together on one XCD and share its L2.  Units
+// are numbered kv head major, then request, so that each XCD's run holds a
+// slice of every request: with requests of different prefix lengths no XCD
+// gets all of the longest one.
 __device__ __forceinline__ bool decode_unit(const FwdParams &p, Unit &u)
 {
     const int w = blockIdx.x;
@@ -92,8 +95,8 @@ __device__ __forceinline__ bool decode_unit(const FwdParams &p, Unit &u)
     int t = id / p.n_rt;
     u.s = t % p.nsplit;
     t /= p.nsplit;
-    u.c = t % p.Hkv;
-    u.b = t / p.Hkv;
+    u.b = t % p.B;
+    u.c = t / p.B;
     return true;
 }
 
@@ -504,8 +507,14 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     const bool row_ok = my_row < rows;
     const int node = row_ok ? my_row / p.G : 0;
     const int qh = u.c * p.G + (row_ok ? my_row - node * p.G : 0);
-    // (an empty prefix split, past its request's prefix, runs no key block:
-    // its rows' partial lse is -inf, so the merge gives it zero weight)
+    if (!R.owns_tree && R.kend <= R.kstart) {
+        // an empty prefix split (past its request's prefix): its rows'
+        // partial lse is -inf, so the merge gives it zero weight and never
+        // reads its partial output
+        if (row_ok && hh == 0 && ks == 0)
+            gmem((f32x2 *)p.ws_ml)[((int64_t)u.s * p.N + R.off + node) * p.Hq + qh] = f32x2{-INFINITY, 0.f};
+        return;   // uniform across the workgroup
+    }
     const int c = u.c;
     const int64_t head_off = (int64_t)c * D;
     const int64_t row_stride = (int64_t)p.Hkv * D;   // elements between key rows

@@ -111,8 +111,15 @@ Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tre
             const int64_t base = (int64_t)B * Hkv * g.n_rt;
             // one workgroup per CU for the 4-wave budget-16 shape: more,
             // smaller prefix chunks cost more in the merge than they gain
-            // (17 slots against 33 at chain16: 17.6 against 23.4 us a step)
-            const int64_t target = (g.nr == 2 && D == 128) ? kNumCUs : kNumCUs * (kWavesPerCU / nw);
+            // (17 slots against 33 at chain16: 12.5 against 15.5 us a step)
+            int64_t target = (g.nr == 2 && D == 128) ? kNumCUs : kNumCUs * (kWavesPerCU / nw);
+            // With several requests the prefixes can differ in length, and
+            // chunks are cut to the longest: finer chunks keep the long
+            // requests' units from trailing the rest (8 requests of 512 to
+            // 4051 keys, budget 64: 6 slots 42.4 us against 4 slots 52.5 us
+            // for the attention kernel)
+            if (B > 1)
+                target = target * 3 / 2;
             if (base > 0 && base < target)
                 nslot = ceil_div(target, base);
         }
