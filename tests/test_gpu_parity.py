@@ -176,6 +176,10 @@ def small_cases():
         # enough (request, kv head, 128-row) units for the 4-wave workgroups
         ("wide-batch", [int(x) for x in rng.integers(1, 400, 16)],
          [W.best_first_tree(64, rng) for _ in range(16)], dict(Hq=32, Hkv=8)),
+        # at least 4096 (node, head) rows: the merge takes lanes per row for
+        # up to 16 splits (head_dim 64: 8 lanes per row)
+        ("many-rows-d64", [900, 2100], [W.best_first_tree(128, rng), W.best_first_tree(100, rng)],
+         dict(Hq=32, Hkv=8, D=64)),
         # <= 32 rows per kv head with long prefixes: one row tile, so a wave's
         # copy rows of a full prefix block span two 16-row page groups
         # (head_dim 128: four key slices; head_dim 64: two)
@@ -195,7 +199,7 @@ def test_fwd_small_cases(dev, idx):
     name, prefix, trees, kw = CASES[idx]
     w = small(name, prefix, trees, seed=100 + idx, **kw)
     o_ref, l_ref = oracle.tree_attn_workload(w)
-    splits = (0, 1, 3, 64) if w.dtype == torch.bfloat16 and w.max_prefix > 0 else (0,)
+    splits = (0, 1, 3, 12, 64) if w.dtype == torch.bfloat16 and w.max_prefix > 0 else (0,)
     for ns in splits:
         out, lse = gpu_fwd(w, dev, num_splits=ns)
         assert_close(w, out, lse, o_ref, l_ref, f"{name} splits={ns}")
@@ -222,23 +226,31 @@ def test_large_and_jumping_scores(dev, dtype):
         assert_close(w, out, lse, o_ref, l_ref, f"rescale {dtype} splits={ns}")
 
 
+@pytest.mark.parametrize("rows", ["few", "many"])
 @pytest.mark.parametrize("log2_scale", [13, 17, 60, -60])
-def test_large_values_through_fp16_partials(dev, log2_scale):
+def test_large_values_through_fp16_partials(dev, log2_scale, rows):
     """Split calls keep each split's normalised partial output in fp16, each
     row scaled by a power of two so that its largest magnitude is in [2^14,
     2^15).  V scaled by 2^13 (|V| up to about 4e4), 2^17 (about 6e5, beyond
     the fp16 range), 2^60 (about 1e19) and 2^-60 (below the smallest fp16
     subnormal) -- all exact in bf16 -- must still match the oracle through
-    splits 5, 17 and 64, compared in units of the scale."""
+    splits 5, 12, 17 and 64, compared in units of the scale; with few rows
+    (one wave per row in the merge) and with many (lanes per row up to 16
+    splits)."""
     rng = W.rng_for(23, 0)
-    w = small("large-v", [1500, 300], [W.chain(16), W.best_first_tree(40, rng)], seed=23)
+    if rows == "few":
+        w = small("large-v", [1500, 300], [W.chain(16), W.best_first_tree(40, rng)], seed=23)
+    else:
+        w = small("large-v-rows", [1500, 300], [W.best_first_tree(100, rng), W.best_first_tree(60, rng)],
+                  Hq=32, Hkv=8, seed=23)
+        assert w.N * w.Hq >= 4096
     scale = 2.0 ** log2_scale
     w.v_cache = (w.v_cache.float() * scale).to(torch.bfloat16)    # sentinel NaN slots stay NaN
     w.v_tree = (w.v_tree.float() * scale).to(torch.bfloat16)
     vmax = max(torch.nan_to_num(w.v_cache.float()).abs().max().item(), w.v_tree.float().abs().max().item())
     assert 2.0 ** (log2_scale + 1) < vmax < 2.0 ** (log2_scale + 4)
     o_ref, l_ref = oracle.tree_attn_workload(w)
-    for ns in (0, 5, 17, 64):
+    for ns in (0, 5, 12, 17, 64):
         out, lse = gpu_fwd(w, dev, num_splits=ns)
         assert_close(w, out / scale, lse, np.asarray(o_ref) / scale, l_ref,
                      f"V * 2^{log2_scale} splits={ns}")

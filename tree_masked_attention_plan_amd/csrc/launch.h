@@ -15,6 +15,7 @@ constexpr int kTreeBadOffsets = -1;
 constexpr int kTreeBadPrefix = -2;
 constexpr int kBlockKeys = 64;   // keys per LDS block of the forward kernel
 constexpr int kMaxSplits = 64;   // merge uses one lane per split
+constexpr int64_t kMergeLanesMinRows = 4096;   // merge: lanes per row from here on
 
 struct PlanParams {
     const int32_t *parent;
