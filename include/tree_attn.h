@@ -276,7 +276,9 @@ ta_status_t tree_attn_plan_dfs(const int32_t *parent, const int32_t *tree_off,
  * tree_attn_gather_rows -- dst[i] = src[index[i]] for n_rows rows of
  * row_bytes bytes each (device pointers).  It moves the rows of q, k_tree,
  * v_tree, out or lse between the old and the depth-first labelling of
- * tree_attn_plan_dfs.  An index outside [0, n_src) yields a zero row.
+ * tree_attn_plan_dfs; that the relabelled call gives the same outputs rests
+ * on the mask depending only on root paths (JetFlow technical summary,
+ * section 2, tree-causal attention mask).  An index outside [0, n_src) yields a zero row.
  * row_bytes must be a multiple of 4 and src, dst 4-byte aligned
  * (TA_ERR_BAD_SHAPE / TA_ERR_UNSUPPORTED).  src and dst must not overlap.
  * Enqueued on stream; returns without synchronising.
@@ -292,7 +294,10 @@ ta_status_t tree_attn_gather_rows(const void *src, int64_t n_src, const int32_t 
  * and best-first expansion grows each request's tree to the token budget
  * (JetFlow technical summary, section 2, tree construction).
  *   logp [B, max_depth, K] f32 (device): log-probability of candidate token k
- *        at depth d + 1, shared by every node at depth d.
+ *        at depth d + 1, shared by every node at depth d; every value <= 0,
+ *        -inf or NaN.  Positive values are outside the contract (the trees
+ *        are built depth by depth on the fact that a child never beats its
+ *        parent) and may differ from the expansion below.
  * Expansion: a virtual root (depth 0, score 0) pushes its K children (child
  * k: score logp[b, 0, k], push number k).  Then T times: pop the candidate
  * with the largest score, equal scores going to the smaller push number; it
@@ -363,7 +368,11 @@ ta_status_t tree_attn_commit(const uint64_t *anc_mask, const int32_t *depth, con
  * The two stages of tree_attn_fwd, for callers that schedule or time them
  * separately.  Both take exactly the arguments of tree_attn_fwd and run the
  * same host checks; tree_attn_fwd is tree_attn_fwd_partial followed by
- * tree_attn_merge on the same stream.
+ * tree_attn_merge on the same stream.  Defined by: the tree-causal attention
+ * of tree_attn_fwd (JetFlow technical summary, section 2, core architecture;
+ * section 3, the paged prefix of the industrial integration).  Cutting the
+ * prefix into chunks and merging their softmax by log-sum-exp rewrites the
+ * same sums exactly; the pages state no split of their own.
  *   tree_attn_fwd_partial  launches the attention kernel.  With one prefix
  *                          split it writes out / lse itself; otherwise each
  *                          split writes its scaled partial output and its
@@ -399,7 +408,8 @@ ta_status_t tree_attn_merge(const void *q, const void *k_tree, const void *v_tre
 /*
  * The first stage of tree_attn_plan_fwd, with the same arguments and host
  * checks: the plan and the attention kernel (for fp32 or N = 0, the plan
- * kernel and tree_attn_fwd_partial).  tree_attn_plan_fwd is this followed by
+ * kernel and tree_attn_fwd_partial).  Defined by: as tree_attn_plan_fwd
+ * (JetFlow technical summary, section 2, tree-causal attention mask).  tree_attn_plan_fwd is this followed by
  * tree_attn_merge, called with the tree_attn_fwd arguments of the same call
  * (anc_mask = the mask output).
  */
