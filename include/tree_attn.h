@@ -193,6 +193,9 @@ size_t tree_attn_workspace_bytes(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
  * Supported: dtype bf16 or fp32; D in {64, 128}; page_size a power of two in
  *   [1, 1024]; Hq % Hkv == 0.  Anything else is TA_ERR_UNSUPPORTED or
  *   TA_ERR_BAD_SHAPE.
+ * Alignment: q, k_tree, v_tree, k_cache, v_cache and out 16-byte aligned
+ *   (rows move as 16-byte vectors), anc_mask 8-byte, lse, block_table,
+ *   prefix_len and tree_off 4-byte; TA_ERR_BAD_SHAPE otherwise.
  * Device-side robustness: a page id outside [0, num_pages) or a prefix
  *   longer than the block table makes the kernel skip those keys rather than
  *   read outside the pool; tree sizes above max_tree are clamped.  Such inputs

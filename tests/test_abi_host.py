@@ -137,6 +137,13 @@ def test_fwd_check_accepts_valid_arguments(lib):
     (dict(workspace=None), TA_ERR_WORKSPACE),
     (dict(ws_bytes=1024), TA_ERR_WORKSPACE),
     (dict(workspace=FAKE + 4), TA_ERR_WORKSPACE),
+    # rows move as 16-byte vectors, mask words as u64, the rest as 32-bit words
+    (dict(q=FAKE + 4), TA_ERR_BAD_SHAPE),
+    (dict(k_cache=FAKE + 8), TA_ERR_BAD_SHAPE),
+    (dict(v_tree=FAKE + 2), TA_ERR_BAD_SHAPE),
+    (dict(out=FAKE + 12), TA_ERR_BAD_SHAPE),
+    (dict(anc_mask=FAKE + 4), TA_ERR_BAD_SHAPE),
+    (dict(lse=FAKE + 2), TA_ERR_BAD_SHAPE),
 ])
 def test_fwd_check_rejects(lib, over, code):
     assert check(lib, **over) == code

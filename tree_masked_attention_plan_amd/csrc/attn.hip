@@ -1358,14 +1358,22 @@ __global__ __launch_bounds__(256) void merge_lanes_kernel(FwdParams p_arg)
 }
 
 // ---------------------------------------------------------------------------
-// fp32 forward: one wave per (node, q head) row; lanes take keys for the
-// scores and head-dim elements for the output.  No split (nsplit == 1).
+// fp32 forward: one wave per (node, q head) row, 64 keys per step.  Lanes
+// take keys for the scores (each lane's K row read as 16-byte vectors, all in
+// flight, four partial dot products), the softmax reductions run on DPP and
+// lane swaps, the visible keys' weights and rows are compacted in LDS, and
+// lanes take head-dim elements for P V with 32 / (D / 64) V rows in flight.
+// No split (nsplit == 1).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p)
 {
     constexpr int PER = D / 64;
-    __shared__ float qs[4][D];
+    constexpr int D4 = D / 4;
+    constexpr int U = 32 / PER;   // V rows in flight (32 registers of them)
+    __shared__ float4 qs[4][D4];
+    __shared__ float pl[4][64];
+    __shared__ int64_t rl[4][64];
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
@@ -1376,12 +1384,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p)
     const bool live = node < R.T;
     const int c = qh / p.G;
     const int64_t n = R.off + (live ? node : 0);
-    if (live) {
-        const float *q = (const float *)p.q + (n * p.Hq + qh) * D;
-#pragma unroll
-        for (int e = 0; e < PER; ++e)
-            qs[wv][lane + 64 * e] = q[lane + 64 * e];
-    }
+    if (live && lane < D4)
+        qs[wv][lane] = ((const float4 *)p.q)[(n * p.Hq + qh) * D4 + lane];
     __syncthreads();
     if (!live)
         return;   // no barrier after this point
@@ -1391,6 +1395,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p)
     const float *vc_base = (const float *)p.v_cache;
     const float *kt_base = (const float *)p.k_tree;
     const float *vt_base = (const float *)p.v_tree;
+    auto fmax_op = [](float a, float x) { return fmaxf(a, x); };
+    auto add_op = [](float a, float x) { return a + x; };
 
     float m_run = -INFINITY, l_run = 0.f;
     float acc[PER];
@@ -1414,39 +1420,58 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p)
         const float *vb = is_tree ? vt_base : vc_base;
         float s = -INFINITY;
         if (r >= 0) {
-            float d0 = 0.f;
-            const float *kr = kb + r;
-            for (int d = 0; d < D; ++d)
-                d0 = __builtin_fmaf(qs[wv][d], kr[d], d0);
-            s = d0 * p.c2;
-        }
-        float mx = s;
+            const float4 *kr = (const float4 *)(kb + r);
+            float4 kv[D4];
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1)
-            mx = fmaxf(mx, __shfl_xor(mx, o));
+            for (int i = 0; i < D4; ++i)
+                kv[i] = kr[i];
+            float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < D4; ++i) {
+                const float4 qv = qs[wv][i];
+                float &a = a4[i & 3];
+                a = __builtin_fmaf(qv.x, kv[i].x, a);
+                a = __builtin_fmaf(qv.y, kv[i].y, a);
+                a = __builtin_fmaf(qv.z, kv[i].z, a);
+                a = __builtin_fmaf(qv.w, kv[i].w, a);
+            }
+            s = ((a4[0] + a4[1]) + (a4[2] + a4[3])) * p.c2;
+        }
+        const float mx = wave_reduce(s, fmax_op);
         const float m_new = fmaxf(m_run, mx);
         if (m_new == -INFINITY)
             continue;   // nothing visible yet in this chunk or before
         const float alpha = fast_exp2(m_run - m_new);
         const float pv = (r >= 0) ? fast_exp2(s - m_new) : 0.f;
-        float ps = pv;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1)
-            ps += __shfl_xor(ps, o);
-        l_run = l_run * alpha + ps;
+        l_run = l_run * alpha + wave_reduce(pv, add_op);
 #pragma unroll
         for (int e = 0; e < PER; ++e)
             acc[e] *= alpha;
-        uint64_t vis = __ballot(r >= 0);
-        while (vis) {
-            const int jl = __builtin_ctzll(vis);
-            vis &= vis - 1;
-            const float pj = __shfl(pv, jl);
-            const int64_t rj = __shfl(r, jl);
-            const float *vr = vb + rj;
+        // the visible keys of this step, compacted in lane order
+        const uint64_t vis = __ballot(r >= 0);
+        const int nvis = __builtin_popcountll(vis);
+        if (r >= 0) {
+            const int idx = __builtin_popcountll(vis & ((1ull << lane) - 1ull));
+            pl[wv][idx] = pv;
+            rl[wv][idx] = r;
+        }
+        for (int j0 = 0; j0 < nvis; j0 += U) {
+            float pj[U];
+            float v[U][PER];
 #pragma unroll
-            for (int e = 0; e < PER; ++e)
-                acc[e] = __builtin_fmaf(pj, vr[lane + 64 * e], acc[e]);
+            for (int u = 0; u < U; ++u) {
+                const int jj = min(j0 + u, nvis - 1);   // past the end: a visible row, weight 0
+                pj[u] = j0 + u < nvis ? pl[wv][jj] : 0.f;
+                const float *vr = vb + rl[wv][jj];
+#pragma unroll
+                for (int e = 0; e < PER; ++e)
+                    v[u][e] = vr[lane + 64 * e];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < PER; ++e)
+                    acc[e] = __builtin_fmaf(pj[u], v[u][e], acc[e]);
         }
         m_run = m_new;
     }

@@ -203,6 +203,14 @@ ta_status_t check_fwd(const void *q, const void *k_tree, const void *v_tree, con
         return TA_ERR_NULL_PTR;
     if (max_prefix > 0 && (!k_cache || !v_cache || !block_table))
         return TA_ERR_NULL_PTR;
+    // the kernels move rows of q, k, v and out as 16-byte vectors, mask words
+    // as u64 and the rest as 32-bit words
+    for (const void *ptr : {q, k_tree, v_tree, k_cache, v_cache, out})
+        if (((uintptr_t)ptr & 15) != 0)
+            return TA_ERR_BAD_SHAPE;
+    if (((uintptr_t)anc_mask & 7) != 0 || ((uintptr_t)lse & 3) != 0 || ((uintptr_t)block_table & 3) != 0 ||
+        ((uintptr_t)prefix_len & 3) != 0 || ((uintptr_t)tree_off & 3) != 0)
+        return TA_ERR_BAD_SHAPE;
     const Geometry g = geometry(B, Hq, Hkv, D, max_tree, max_prefix, dtype, num_splits);
     const size_t need = ws_bytes(g, N, Hq, D);
     if (need > 0) {
