@@ -180,6 +180,14 @@ def small_cases():
         # up to 16 splits (head_dim 64: 8 lanes per row)
         ("many-rows-d64", [900, 2100], [W.best_first_tree(128, rng), W.best_first_tree(100, rng)],
          dict(Hq=32, Hkv=8, D=64)),
+        # the largest page size: a 64-key block inside one page, three pages
+        # for the longest prefix
+        ("page1024", [3000, 500], [W.best_first_tree(30, rng), W.chain(8)], dict(ps=1024)),
+        ("page256-d64", [700, 1], [W.random_tree(50, 10, rng), W.chain(2)], dict(ps=256, D=64)),
+        ("fp32-page1024", [1500], [W.best_first_tree(20, rng)], dict(dtype=torch.float32, ps=1024)),
+        # many small requests: hundreds of work units of one row tile each
+        ("many-small-requests", [int(x) for x in rng.integers(0, 41, 300)],
+         [W.random_tree(int(t), 3, rng) for t in rng.integers(1, 5, 300)], {}),
         # <= 32 rows per kv head with long prefixes: one row tile, so a wave's
         # copy rows of a full prefix block span two 16-row page groups
         # (head_dim 128: four key slices; head_dim 64: two)

@@ -42,11 +42,20 @@ def check(lp, T, dev, what):
 
 
 @pytest.mark.parametrize("K,Dmax,T", [(8, 16, 256), (8, 16, 16), (2, 16, 200), (3, 4, 120), (16, 8, 256),
-                                      (64, 4, 256), (8, 1, 8), (1, 64, 64)])
+                                      (64, 4, 256), (8, 1, 8), (1, 64, 64),
+                                      # the limits: K * max_depth = 4096, K * (T + 1) = 16448
+                                      (64, 64, 256), (16, 64, 256)])
 def test_random_candidates(dev, K, Dmax, T):
     rng = np.random.default_rng(K * 1000 + Dmax * 10 + T)
     lp = logsoftmax(rng.normal(0, 2, size=(6, Dmax, K)))
     check(lp, T, dev, "random")
+
+
+def test_many_requests(dev):
+    """300 requests in one launch (one workgroup each)."""
+    rng = np.random.default_rng(31)
+    lp = logsoftmax(rng.normal(0, 2, size=(300, 16, 8)))
+    check(lp, 64, dev, "many requests")
 
 
 def test_ties_give_breadth_first_order(dev):
