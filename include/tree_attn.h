@@ -123,10 +123,12 @@ ta_status_t tree_attn_plan(const int32_t *parent, const int32_t *tree_off,
  * Number of split slots (split-K, merged by LSE) that tree_attn_fwd uses for
  * these sizes when num_splits = 0 is passed; a pure function of its
  * arguments.  Returns 0 for invalid sizes.  With one slot a single pass covers
- * the prefix and the tree.  With S > 1 slots, slots 0 .. S-2 each cover one
- * chunk of the prefix and slot S-1 covers the tree alone, so the tree phase
- * runs beside the prefix chunks; a forced count is reduced so that every
- * prefix chunk holds at least one 64-key block of the longest prefix.
+ * the prefix and the tree.  With S > 1 slots the slots cover the prefix in
+ * equal chunks; for a single request (B = 1) slot S-1 covers the tree alone,
+ * so the tree phase runs beside the prefix chunks, and with several requests
+ * each request's tree goes with its last non-empty chunk.  A forced count is
+ * reduced so that every prefix chunk holds at least one 64-key block of the
+ * longest prefix.
  */
 int32_t tree_attn_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                              int32_t max_tree, int32_t max_prefix, ta_dtype_t dtype);

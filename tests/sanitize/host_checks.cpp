@@ -83,7 +83,12 @@ int main()
                     const char *l0 = (const char *)p.ws_ml;
                     CHECK(o0 >= ws && o0 + (size_t)p.nsplit * s.N * s.Hq * s.D * 2 <= l0);
                     CHECK(l0 + (size_t)p.nsplit * s.N * s.Hq * 8 <= ws + need);
-                    CHECK(p.chunk > 0 && (int64_t)p.chunk * (p.nsplit - 1) >= s.maxpre);
+                    // the prefix slots (all but the tree's own slot, if any)
+                    // cover the longest prefix, and none is empty for it
+                    const int npre = p.nsplit - (p.tree_slot ? 1 : 0);
+                    CHECK(p.tree_slot == (s.B <= 1 ? 1 : 0));
+                    CHECK(p.chunk > 0 && (int64_t)p.chunk * npre >= s.maxpre);
+                    CHECK((int64_t)p.chunk * (npre - 1) < s.maxpre);
                 }
                 CHECK(p.units > 0 && p.units_per_xcd * 8 >= p.units);
                 if (need > 0) {

@@ -75,7 +75,7 @@ __device__ __forceinline__ FwdParams load_args(const FwdParams &in)
                       "+s"(a.out), "+s"(a.lse), "+s"(a.ws_o), "+s"(a.ws_ml));
     asm volatile("" : "+s"(a.B), "+s"(a.N), "+s"(a.Hq), "+s"(a.Hkv), "+s"(a.G), "+s"(a.D),
                       "+s"(a.num_pages), "+s"(a.max_pages), "+s"(a.page_shift), "+s"(a.max_tree),
-                      "+s"(a.nsplit), "+s"(a.chunk), "+s"(a.n_rt), "+s"(a.units),
+                      "+s"(a.nsplit), "+s"(a.chunk), "+s"(a.tree_slot), "+s"(a.n_rt), "+s"(a.units),
                       "+s"(a.units_per_xcd), "+s"(a.c2));
     return a;
 }
@@ -108,9 +108,11 @@ struct ReqInfo {
 
 // Request geometry, clamped so that no input can drive an access outside the
 // caller's buffers.  With one split the unit covers the whole prefix and the
-// tree.  With nsplit > 1 the last split slot holds the tree phase alone and
-// slots 0 .. nsplit-2 cover the prefix in chunks of `chunk` keys (a slot past
-// the request's prefix is empty).
+// tree.  With nsplit > 1, slot s covers prefix keys [s * chunk, (s + 1) *
+// chunk) (a slot past the request's prefix is empty), and the tree phase goes
+// either to a slot of its own, the last (tree_slot: the tree runs beside the
+// prefix chunks), or to the request's last non-empty chunk (slot 0 for an
+// empty prefix).
 __device__ __forceinline__ ReqInfo request_info(const FwdParams &p, int b, int s)
 {
     // read-only for the whole launch: scalar loads through the constant space
@@ -129,14 +131,14 @@ __device__ __forceinline__ ReqInfo request_info(const FwdParams &p, int b, int s
         r.kstart = 0;
         r.kend = L;
         r.owns_tree = true;
-    } else if (s == p.nsplit - 1) {
+    } else if (p.tree_slot && s == p.nsplit - 1) {
         r.kstart = 0;
         r.kend = 0;
         r.owns_tree = true;
     } else {
         r.kstart = s * p.chunk;
         r.kend = max(r.kstart, min(L, r.kstart + p.chunk));
-        r.owns_tree = false;
+        r.owns_tree = !p.tree_slot && s == (L > 0 ? (L - 1) / p.chunk : 0);
     }
     return r;
 }

@@ -64,7 +64,10 @@ struct FwdParams {
                        // scores, e) per partial row
     int32_t B, N, Hq, Hkv, G, D;
     int32_t num_pages, max_pages, page_shift, max_tree;
-    int32_t nsplit, chunk;          // prefix split count and keys per split
+    int32_t nsplit, chunk;          // split slots and prefix keys per slot
+    int32_t tree_slot;              // 1: with nsplit > 1 the last slot runs the
+                                    // tree alone; 0: a request's tree rides with
+                                    // its last non-empty prefix chunk
     int32_t n_rt;                   // row tiles per (request, kv head)
     int32_t units, units_per_xcd;   // work units and their per-XCD share
     float c2;                       // softmax scale * log2(e)

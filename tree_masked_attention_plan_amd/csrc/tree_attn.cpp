@@ -50,6 +50,7 @@ int32_t waves_for(int32_t rows)
 
 struct Geometry {
     int32_t nr, ks, n_rt, nsplit, chunk;
+    bool tree_slot;   // nsplit > 1: the last slot runs the tree alone
 };
 
 // key slices per row tile (waves of one row tile that split each step's
@@ -76,12 +77,15 @@ bool sizes_ok(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tree, i
 }
 
 // Work decomposition: row tiles per (request, kv head) and split slots.
-// With more than one slot, the last slot runs the tree phase alone and the
-// others cover the prefix in equal chunks of whole 64-key blocks, so that the
-// tree and the prefix chunks run side by side.  Slots are added only while
-// the grid is short of one full wave of the GPU, and are re-counted after
-// rounding the chunk to whole blocks so that no trailing prefix slot is empty
-// for the longest prefix.
+// The prefix is cut into equal chunks of whole 64-key blocks, one fewer than
+// the slot target.  For a single request the last slot runs the tree phase
+// alone, beside the prefix chunks.  With several requests that slot is
+// dropped and each request's tree rides with its last, partial prefix chunk
+// (8 requests of up to 4051 keys, budget 64: 5 chunks and no tree slot,
+// attention kernel 39.9 us, against 42.4 us with a tree slot per request).
+// Slots are added only while the grid is short of one full wave of the GPU,
+// and are re-counted after rounding the chunk to whole blocks so that no
+// trailing prefix slot is empty for the longest prefix.
 Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tree,
                   int32_t max_prefix, ta_dtype_t dtype, int32_t forced_splits)
 {
@@ -116,8 +120,8 @@ Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tre
             // With several requests the prefixes can differ in length, and
             // chunks are cut to the longest: finer chunks keep the long
             // requests' units from trailing the rest (8 requests of 512 to
-            // 4051 keys, budget 64: 6 slots 42.4 us against 4 slots 52.5 us
-            // for the attention kernel)
+            // 4051 keys, budget 64: 5 prefix chunks, attention kernel 39.9 us,
+            // against 3 chunks 52.5 us and 7 chunks 46.3 us)
             if (B > 1)
                 target = target * 3 / 2;
             if (base > 0 && base < target)
@@ -128,8 +132,11 @@ Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tre
     }
     g.chunk = (int32_t)(ceil_div(max_prefix > 0 ? max_prefix : 1, step_keys) * step_keys);
     g.nsplit = 1;
+    g.tree_slot = B <= 1;
     if (nslot > 1) {
-        int64_t npre = nslot - 1;
+        // prefix chunks: one fewer than the slots, except that a forced count
+        // without a tree slot is all prefix chunks
+        int64_t npre = (forced_splits > 0 && !g.tree_slot) ? nslot : nslot - 1;
         const int64_t max_blocks = ceil_div(max_prefix, ta::kBlockKeys);
         if (npre > max_blocks)
             npre = max_blocks;
@@ -138,7 +145,7 @@ Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tre
         const int64_t unit = per >= step_keys ? step_keys : ta::kBlockKeys;
         int64_t chunk = ceil_div(per, unit) * unit;
         npre = ceil_div(max_prefix, chunk);
-        g.nsplit = (int32_t)(npre + 1);
+        g.nsplit = (int32_t)(g.tree_slot ? npre + 1 : npre);
         g.chunk = (int32_t)chunk;
     }
     return g;
@@ -504,6 +511,7 @@ ta_status_t run_fwd(const void *q, const void *k_tree, const void *v_tree, const
     p.max_tree = max_tree;
     p.nsplit = g.nsplit;
     p.chunk = g.chunk;
+    p.tree_slot = g.tree_slot ? 1 : 0;
     p.n_rt = g.n_rt;
     p.units = (int32_t)units;
     p.units_per_xcd = (int32_t)ceil_div(units, 8);
