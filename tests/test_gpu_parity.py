@@ -297,6 +297,53 @@ def test_non_default_stream_and_determinism(dev):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_concurrent_host_threads(dev):
+    """The library keeps no state, so calls are reentrant: two host threads,
+    each on its own stream with its own workload and split workspace, issue
+    calls at the same time; every result equals the same call made alone,
+    bit for bit."""
+    import threading
+    rng = W.rng_for(17, 0)
+    ws = [small("threads-a", [1800, 60], [W.chain(16), W.best_first_tree(50, rng)], seed=17),
+          small("threads-b", [900], [W.best_first_tree(120, rng)], D=64, seed=18)]
+    ref = []
+    for w in ws:
+        o, l = gpu_fwd(w, dev, num_splits=5)
+        torch.cuda.synchronize()
+        ref.append((o.clone(), l.clone()))
+    wds = [w.to(dev) for w in ws]
+    plans = [ta.plan(wd.parent, wd.tree_off, wd.prefix_len, max_tree=w.max_tree) for w, wd in zip(ws, wds)]
+    torch.cuda.synchronize()
+    results = [[None] * 8 for _ in ws]
+    errors = []
+    start = threading.Barrier(len(ws))
+
+    def worker(i):
+        try:
+            w, wd, res = ws[i], wds[i], plans[i]
+            st = torch.cuda.Stream(dev)
+            start.wait()
+            with torch.cuda.stream(st):
+                for r in range(8):
+                    results[i][r] = ta.fwd(wd.q, wd.k_tree, wd.v_tree, wd.k_cache, wd.v_cache, wd.block_table,
+                                           wd.prefix_len, wd.tree_off, res.anc_mask, max_tree=w.max_tree,
+                                           max_prefix=w.max_prefix, num_splits=5, stream=st)
+            st.synchronize()
+        except Exception as e:   # reported below, on the test's thread
+            errors.append(e)
+
+    say("two host threads, one stream each, 8 calls each")
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(ws))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    for i, (o_ref, l_ref) in enumerate(ref):
+        for o, l in results[i]:
+            assert torch.equal(o.float().cpu().double(), o_ref) and torch.equal(l.cpu().double(), l_ref)
+
+
 def test_side_stream_keeps_workspace_alive(dev):
     """A forward call enqueued on a side stream from outside that stream's
     context, with the library-allocated split workspace: once the call
