@@ -264,6 +264,37 @@ def test_large_values_through_fp16_partials(dev, log2_scale, rows):
                      f"V * 2^{log2_scale} splits={ns}")
 
 
+def random_config(i):
+    """A seeded random shape: batch, tree kinds and sizes, prefix lengths,
+    GQA ratio, head dim, page size, dtype and a forced split count, sized so
+    that the oracle finishes in about a second."""
+    rng = np.random.default_rng(5000 + i)
+    B = int(rng.integers(1, 7))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 5, 8]))
+    D = int(rng.choice([64, 128]))
+    ps = int(rng.choice([1, 4, 16, 32, 64, 256, 1024]))
+    dtype = torch.float32 if rng.random() < 0.2 else torch.bfloat16
+    trees, prefix = [], []
+    for _ in range(B):
+        T = int(rng.integers(0, 257)) if rng.random() < 0.3 else int(rng.integers(1, 65))
+        kind = rng.integers(0, 3) if T > 0 else 0
+        trees.append(W.chain(T) if kind == 0 else
+                     (W.random_tree(T, int(rng.integers(2, 17)), rng) if kind == 1 else W.best_first_tree(T, rng)))
+        prefix.append(int(rng.integers(0, 3000)) if rng.random() < 0.85 else 0)
+    splits = int(rng.choice([0, 0, 1, 2, 7, 64])) if dtype == torch.bfloat16 else 0
+    return f"random-{i}", prefix, trees, dict(Hq=G * Hkv, Hkv=Hkv, D=D, dtype=dtype, ps=ps), splits
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_configurations(dev, i):
+    name, prefix, trees, kw, splits = random_config(i)
+    w = small(name, prefix, trees, seed=700 + i, **kw)
+    o_ref, l_ref = oracle.tree_attn_workload(w)
+    out, lse = gpu_fwd(w, dev, num_splits=splits)
+    assert_close(w, out, lse, o_ref, l_ref, f"{name} splits={splits}")
+
+
 def test_softmax_scale_override(dev):
     rng = W.rng_for(8, 0)
     w = small("scale", [90], [W.best_first_tree(30, rng)], seed=8)
