@@ -18,7 +18,7 @@ import torch
 import oracle
 import tree_masked_attention_plan_amd as ta
 from tree_masked_attention_plan_amd import workloads as W
-from tests.test_gpu_parity import CASES, assert_close, small
+from tests.test_gpu_parity import CASES, assert_close, random_config, small
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +86,17 @@ def test_small_cases(dev, idx):
         plan, out, lse = run(w, dev, num_splits=ns)
         check_plan(plan, w.parent, w.tree_off, w.prefix_len, w.max_tree, f"{name} splits={ns}")
         assert_close(w, out, lse, o_ref, l_ref, f"{name} splits={ns}")
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_configurations(dev, i):
+    """The seeded random shapes of the forward tests, through the one call."""
+    name, prefix, trees, kw, splits = random_config(i)
+    w = small(name, prefix, trees, seed=700 + i, **kw)
+    o_ref, l_ref = oracle.tree_attn_workload(w)
+    plan, out, lse = run(w, dev, num_splits=splits)
+    check_plan(plan, w.parent, w.tree_off, w.prefix_len, w.max_tree, name)
+    assert_close(w, out, lse, o_ref, l_ref, f"{name} one call, splits={splits}")
 
 
 @pytest.mark.parametrize("num_splits", [1, 4])
