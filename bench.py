@@ -10,7 +10,7 @@ from HIP graphs holding one step per input replica (a replica cycle; a step
 count short of a cycle replays a graph of the remaining steps, captured
 beforehand), and successive steps rotate over enough replicas that the
 working set does not stay in the 256 MB Infinity Cache.  Before any timing,
-at least 0.5 s of untimed steps bring the clocks up (and keep the GPU
+at least 1.5 s of untimed steps bring the clocks up (and keep the GPU
 visibly busy to an outside utilisation sampler), whatever ``--warmup`` says; then ``--warmup`` untimed steps, then exactly ``--steps`` steps timed
 with HIP events on the replay stream.  ``value`` is tree tokens per second of
 that GPU time.
@@ -223,7 +223,7 @@ class Runner:
             self.rest[k % R].replay()
 
 
-def ramp_clocks(runner: Runner, seconds: float = 0.5) -> float:
+def ramp_clocks(runner: Runner, seconds: float = 1.5) -> float:
     """Untimed GPU work before any timing (whatever --warmup says): whole
     replica cycles until at least ``seconds`` of GPU time have passed, so
     that the timed steps do not catch the clocks ramping up.  Returns the
