@@ -207,12 +207,16 @@ class Runner:
 
     def prepare(self, *counts):
         """Capture the remainder graphs that ``run_steps`` needs for these
-        step counts (steps on replicas 0 .. k % R - 1)."""
+        step counts (steps on replicas 0 .. k % R - 1), and replay each new
+        one once, untimed: a graph's first replay also uploads it."""
         R = len(self.reps)
         for k in counts:
             m = k % R
             if m and m not in self.rest:
                 self.rest[m] = capture(lambda: [r.step() for r in self.reps[:m]], 1)
+                self.rest[m].replay()
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(1000)   # load the spin kernel of _busy_stream outside any timing
         torch.cuda.synchronize()
 
     def run_steps(self, k):
@@ -244,10 +248,23 @@ def ramp_clocks(runner: Runner, seconds: float = 1.5) -> float:
     return spent
 
 
+def _busy_stream(runner: Runner):
+    """Untimed GPU work that keeps the stream busy while the host enqueues
+    the start event and the timed steps, so that the GPU does not sit idle
+    between that event and the first timed step (an idle gap of tens of
+    microseconds that a short timed region would otherwise count): a spin
+    of about 100 us, or one replica cycle without it."""
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(200_000)
+    else:
+        runner.chunk.replay()
+
+
 def time_steps(runner: Runner, steps: int, warmup: int) -> tuple:
     """``warmup`` untimed steps, then exactly ``steps`` steps bracketed by
     device synchronisations.  Returns (GPU seconds from HIP events recorded
-    on the replay stream around the steps, host wall seconds)."""
+    on the replay stream around the steps, host wall seconds; the wall time
+    also holds the short untimed spin ahead of the start event)."""
     runner.prepare(steps, warmup)
     runner.run_steps(warmup)
     torch.cuda.synchronize()
@@ -255,6 +272,7 @@ def time_steps(runner: Runner, steps: int, warmup: int) -> tuple:
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    _busy_stream(runner)
     e0.record(stream)
     runner.run_steps(steps)
     e1.record(stream)
@@ -382,6 +400,7 @@ def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: flo
     runner = Runner(reps, compare)
     nsplit = reps[0].call.num_splits
     wk = work(w, nsplit)
+    runner.prepare(steps, warmup)   # before the ramp: no first replay in a timed region
     ramp = ramp_clocks(runner)
     gpu_s, wall_s = time_steps(runner, steps, warmup)
     ms = gpu_s / steps * 1e3
@@ -503,6 +522,8 @@ def time_calls(fn, reps: int, per_graph: int = 20) -> float:
     n = max(1, reps // per_graph)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(200_000)   # the stream busy while the timed replays are enqueued
     e0.record()
     for _ in range(n):
         g.replay()
