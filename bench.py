@@ -680,7 +680,8 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(this path shards by request or kv head with no exchange; see the design notes)",
+              f"(the attention shards by request or by kv head with no exchange between GPUs, so "
+              f"N GPUs run N independent copies of this measurement)",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
