@@ -286,7 +286,7 @@ def random_config(i):
     return f"random-{i}", prefix, trees, dict(Hq=G * Hkv, Hkv=Hkv, D=D, dtype=dtype, ps=ps), splits
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(200))
 def test_random_configurations(dev, i):
     name, prefix, trees, kw, splits = random_config(i)
     w = small(name, prefix, trees, seed=700 + i, **kw)

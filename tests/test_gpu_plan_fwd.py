@@ -88,7 +88,7 @@ def test_small_cases(dev, idx):
         assert_close(w, out, lse, o_ref, l_ref, f"{name} splits={ns}")
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(200))
 def test_random_configurations(dev, i):
     """The seeded random shapes of the forward tests, through the one call."""
     name, prefix, trees, kw, splits = random_config(i)
