@@ -490,6 +490,10 @@ int oracle_commit(const int32_t *parent, const int32_t *tree_off, const int32_t 
  * b * T.  Scores are fp32 sums taken in this order, so any implementation
  * that adds in the same order decides every comparison identically.
  * T must not exceed the number of nodes of the implicit tree.
+ * NaN log-probabilities (outside the pages' definition, which ranks real
+ * scores) are read as "no candidate": a candidate with a NaN score is never
+ * pushed, so it is never popped; when the pool runs dry before T pops, the
+ * remaining nodes are written as missing (parent -1, choice -1, NaN score).
  */
 typedef struct {
     float score;
@@ -563,9 +567,17 @@ int oracle_build_tree(const float *logp, int32_t B, int32_t Dmax, int32_t K, int
         int64_t n = 0;
         for (int32_t k = 0; k < K; ++k) {
             cand_t c = {lp[k], k, -1, 1, k};
-            heap_push(h, &n, c);
+            if (c.score == c.score)
+                heap_push(h, &n, c);
         }
         for (int32_t i = 0; i < T; ++i) {
+            if (n == 0) {
+                /* no candidate left: the node is missing */
+                parent[(int64_t)b * T + i] = -1;
+                choice[(int64_t)b * T + i] = -1;
+                score[(int64_t)b * T + i] = NAN;
+                continue;
+            }
             const cand_t c = heap_pop(h, &n);
             parent[(int64_t)b * T + i] = c.parent;
             choice[(int64_t)b * T + i] = c.k;
@@ -574,7 +586,8 @@ int oracle_build_tree(const float *logp, int32_t B, int32_t Dmax, int32_t K, int
                 for (int32_t k = 0; k < K; ++k) {
                     volatile float s = c.score + lp[(int64_t)c.depth * K + k];
                     cand_t ch = {s, (int64_t)K + (int64_t)K * i + k, i, c.depth + 1, k};
-                    heap_push(h, &n, ch);
+                    if (ch.score == ch.score)
+                        heap_push(h, &n, ch);
                 }
             }
         }

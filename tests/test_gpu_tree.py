@@ -1,8 +1,9 @@
 """GPU parity of tree_attn_build_tree against the oracle's sequential
 best-first expansion: parent ids and candidate choices must be identical and
 scores bit-identical (both sides add the same fp32 values in the same
-order), including exact ties, zero-probability candidates and budgets up to
-the implicit tree's size."""
+order), including exact ties, zero-probability candidates, NaN
+candidates (never chosen; nodes beyond the finite candidates are missing)
+and budgets up to the implicit tree's size."""
 import numpy as np
 import pytest
 import torch
@@ -38,7 +39,9 @@ def check(lp, T, dev, what):
     say(f"  {what}: B={lp.shape[0]} depth={lp.shape[1]} K={lp.shape[2]} T={T}")
     assert np.array_equal(p, p_ref), f"{what}: parents differ at {np.argwhere(p != p_ref)[:4].tolist()}"
     assert np.array_equal(c, c_ref), f"{what}: choices differ"
-    assert np.array_equal(s.view(np.int32), s_ref.view(np.int32)), f"{what}: scores differ"
+    nan = np.isnan(s_ref)
+    assert np.array_equal(np.isnan(s), nan), f"{what}: missing nodes differ"
+    assert np.array_equal(s[~nan].view(np.int32), s_ref[~nan].view(np.int32)), f"{what}: scores differ"
 
 
 @pytest.mark.parametrize("K,Dmax,T", [(8, 16, 256), (8, 16, 16), (2, 16, 200), (3, 4, 120), (16, 8, 256),
@@ -104,6 +107,18 @@ def test_nan_candidates_are_never_chosen(dev):
     assert np.array_equal(p.cpu().numpy(), p_ref)
     assert np.array_equal(c.cpu().numpy(), c_ref)
     assert np.array_equal(s.cpu().numpy().view(np.int32), s_ref.view(np.int32))
+
+
+@pytest.mark.parametrize("frac,K,Dmax,T", [(0.1, 8, 16, 256), (0.5, 8, 16, 256), (0.85, 8, 16, 256),
+                                           (0.6, 3, 6, 120), (0.3, 1, 64, 64), (0.7, 64, 4, 256)])
+def test_nan_candidates_against_the_oracle(dev, frac, K, Dmax, T):
+    """NaN log-probabilities at random places, compared with the oracle run
+    on the same inputs: the denser cases leave requests with fewer finite
+    candidates than the budget, so missing nodes are covered too."""
+    rng = np.random.default_rng(int(frac * 100) * 7 + K + Dmax + T)
+    lp = logsoftmax(rng.normal(0, 2, size=(6, Dmax, K)))
+    lp = np.where(rng.random(size=lp.shape) < frac, np.float32(np.nan), lp).astype(np.float32)
+    check(lp, T, dev, f"NaN fraction {frac}")
 
 
 def test_nan_candidates_can_leave_nodes_missing(dev):

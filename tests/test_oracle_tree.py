@@ -7,7 +7,11 @@ Closed forms and brute force, independent of the heap the oracle uses:
 - on a tiny implicit tree, the popped set is exactly the T best paths by
   score, in descending order (brute-force enumeration of every path);
 - structural invariants: a parent precedes its child, scores never increase
-  in pop order, and each score is its parent's plus one log-probability.
+  in pop order, and each score is its parent's plus one log-probability;
+- NaN log-probabilities (which the pages' ranking of real scores leaves
+  open) mean "no candidate": brute force over the paths whose fp32 score is
+  not NaN gives the popped set, and nodes beyond the finite candidates are
+  written as missing (parent -1, choice -1, NaN score).
 """
 import itertools
 
@@ -100,3 +104,47 @@ def test_rejects_a_budget_larger_than_the_tree():
     with pytest.raises(ValueError):
         oracle.build_tree(lp, 7)        # the implicit tree has 2 + 4 = 6 nodes
     oracle.build_tree(lp, 6)
+
+
+def paths_of(parent, choice, n):
+    paths = []
+    for i in range(n):
+        p = parent[i]
+        paths.append((paths[p] if p >= 0 else ()) + (int(choice[i]),))
+    return paths
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_nan_candidates_by_brute_force(seed):
+    K, Dmax = 3, 4
+    rng = np.random.default_rng(100 + seed)
+    lp = logsoftmax(rng.normal(0, 2, size=(1, Dmax, K)))
+    # NaN at a few (depth, candidate) places, the first at depth 0 so that a
+    # NaN would sit among the earliest candidates of the pool
+    lp[0, 0, rng.integers(K)] = np.nan
+    for _ in range(2):
+        lp[0, rng.integers(1, Dmax), rng.integers(K)] = np.nan
+    allp = [(s, path) for s, path in enumerate_paths(lp[0], Dmax, K) if s == s]
+    assert len(set(s for s, _ in allp)) == len(allp)
+    best = sorted(allp, key=lambda x: -x[0])
+    for T in (1, 4, 9, len(best), len(best) + 7, 120):
+        parent, choice, score = oracle.build_tree(lp, T)
+        m = min(T, len(best))
+        assert paths_of(parent[0], choice[0], m) == [path for _, path in best[:m]]
+        assert np.array_equal(score[0, :m], np.array([s for s, _ in best[:m]], dtype=np.float32))
+        assert (parent[0, m:] == -1).all() and (choice[0, m:] == -1).all()
+        assert np.isnan(score[0, m:]).all()
+
+
+def test_chain_cut_by_a_nan_log_probability():
+    # one candidate per depth, NaN at depth 3: the first three nodes form a
+    # chain and every later node is missing
+    Dmax, T = 8, 8
+    lp = np.full((2, Dmax, 1), -0.5, dtype=np.float32)
+    lp[1, 3, 0] = np.nan
+    parent, choice, score = oracle.build_tree(lp, T)
+    assert parent[0].tolist() == [-1] + list(range(T - 1))
+    assert parent[1].tolist() == [-1, 0, 1] + [-1] * 5
+    assert choice[1].tolist() == [0, 0, 0] + [-1] * 5
+    assert score[1, :3].tolist() == [-0.5, -1.0, -1.5]
+    assert np.isnan(score[1, 3:]).all()
