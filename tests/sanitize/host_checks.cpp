@@ -20,7 +20,7 @@ hipError_t launch_plan_dfs(const PlanDfsParams &, hipStream_t) { ++n_launch; ret
 hipError_t launch_gather(const GatherParams &, hipStream_t) { ++n_launch; return hipSuccess; }
 hipError_t launch_build_tree(const TreeParams &, hipStream_t) { ++n_launch; return hipSuccess; }
 hipError_t launch_commit(const CommitParams &, hipStream_t) { ++n_launch; return hipSuccess; }
-hipError_t launch_fwd(const FwdParams &p, int, int, int, hipStream_t)
+hipError_t launch_fwd(const FwdParams &p, int, int, int, int, hipStream_t)
 {
     ++n_launch;
     last_fwd = p;

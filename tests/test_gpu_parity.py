@@ -195,6 +195,18 @@ def small_cases():
         ("d64-few-rows-long-prefix", [1500], [W.chain(6)], dict(D=64)),
         # pages of 32 tokens: two 16-row groups per page
         ("page32-long-prefix", [2000, 77], [W.best_first_tree(64, rng), W.chain(4)], dict(ps=32)),
+        # 8-wave units (more than 128 rows per kv head) that fill the GPU
+        # without splits, over prefixes of at least 1024 keys: four K/V
+        # stages, copies three steps ahead; ragged prefixes and tree blocks
+        # make the last steps issue fewer copies
+        ("four-stages", [int(x) for x in rng.integers(1024, 1401, 32)],
+         [W.best_first_tree(int(t), rng) for t in rng.integers(129, 201, 32)], dict(Hq=8, Hkv=8)),
+        # the same with units of 0 to 4 steps beside long ones, and pages of
+        # 8 tokens (page ids loaded per lane)
+        ("four-stages-short-units", [0, 5, 70, 130, 200, 1100] + [int(x) for x in rng.integers(0, 1500, 26)],
+         [W.best_first_tree(int(t), rng) for t in rng.integers(129, 257, 32)], dict(Hq=8, Hkv=8, ps=8)),
+        ("four-stages-page256", [int(x) for x in rng.integers(900, 1300, 32)],
+         [W.random_tree(int(t), 12, rng) for t in rng.integers(129, 180, 32)], dict(Hq=8, Hkv=8, ps=256)),
     ]
     return cases
 

@@ -405,7 +405,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 // serialise a block's copy issue and math.
 // SP: pages hold >= 16 tokens, so a 64-key block spans at most 4 pages whose
 // ids are fetched with scalar loads; otherwise each lane loads its own.
-template <int D, int NR, int KS, bool SP>
+// NSTG: K/V stages in LDS; a step's copies are issued NSTG - 1 steps ahead.
+// Four stages (one key slice only) need 128 KiB at head_dim 128, so one
+// workgroup per CU.
+template <int D, int NR, int KS, bool SP, int NSTG>
 __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdParams p_arg)
 {
     const FwdParams p = load_args(p_arg);
@@ -427,14 +430,14 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     static_assert(NI % NW == 0 && NIW >= 1, "waves must divide the DMA instructions of a step");
     static_assert(NW % KSB == 0, "a wave's DMA instructions must fall in one block");
     static_assert(NDT % KS == 0, "key slices must divide the output d tiles");
+    // with more than two stages every wave issues every step's copies (one
+    // key slice), which the exact copy count waited for at a step relies on
+    static_assert(NSTG == 2 || (NSTG == 4 && KS == 1), "stage counts: 2, or 4 with one key slice");
 
-    // two stages of K and V; after the key loop the same memory holds the
-    // key slices' partial outputs for the combine
-    __shared__ __attribute__((aligned(1024))) char kv_lds[4 * SBYTES];
-    char *const k_st0 = kv_lds;
-    char *const v_st0 = kv_lds + SBYTES;
-    char *const k_st1 = kv_lds + 2 * SBYTES;
-    char *const v_st1 = kv_lds + 3 * SBYTES;
+    // NSTG stages of K and V (stage s: K at 2 s, V at 2 s + 1, in units of
+    // SBYTES); after the key loop the same memory holds the key slices'
+    // partial outputs for the combine
+    __shared__ __attribute__((aligned(1024))) char kv_lds[2 * NSTG * SBYTES];
     // running (max, sum) of every slice's rows, for the final combine, and
     // the largest magnitude of each slice's share of a partial row
     __shared__ float2 ml_x[KS > 1 ? NR * KS * 32 : 1];
@@ -614,8 +617,8 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
             return;
         bool is_tree;
         const int start = block_start(k, is_tree);
-        char *kst = (decltype(stage)::value == 0 ? k_st0 : k_st1) + dma_blk * LY::BLK;
-        char *vst = (decltype(stage)::value == 0 ? v_st0 : v_st1) + dma_blk * LY::BLK;
+        char *kst = kv_lds + 2 * decltype(stage)::value * SBYTES + dma_blk * LY::BLK;
+        char *vst = kst + SBYTES;
         const uint16_t *kb = (const uint16_t *)(is_tree ? kt_p : kc_p);
         const uint16_t *vb = (const uint16_t *)(is_tree ? vt_p : vc_p);
         if (SP && !is_tree && !FIRST && start + 64 <= R.kend) {
@@ -932,27 +935,43 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     const float c2 = p.c2;
 
     // one step: wait for this step's DMA, one barrier (every wave's copy has
-    // landed and every wave has finished the step before), start the next
-    // step's DMA into the other stage, then the math on this stage.  One
-    // barrier per step suffices with two stages because the next copy is
-    // issued only after it.
+    // landed and every wave has finished the step before), start the DMA of
+    // step j + NSTG - 1 into the stage read in step j - 1, then the math on
+    // this stage.  One barrier per step suffices because a stage is refilled
+    // only after it.
     auto step = [&](int j, auto stage) {
-        TA_WAIT_VMCNT(0);                       // this wave's step-j DMA has landed
+        if constexpr (NSTG == 2) {
+            TA_WAIT_VMCNT(0);                   // this wave's step-j DMA has landed
+        } else {
+            // The copies of steps j + 1 .. j + NSTG - 2 (those below n_steps,
+            // 2 NIW instructions each) may stay in flight: copies complete
+            // in issue order, so then step j's have landed.  A vector load
+            // of the compiler's own issued in between only makes this wait
+            // stricter.
+            static_assert(NSTG == 4, "the waits below are written for four stages");
+            const int ahead = n_steps - 1 - j;
+            if (ahead >= 2)
+                TA_WAIT_VMCNT(4 * NIW);
+            else if (ahead == 1)
+                TA_WAIT_VMCNT(2 * NIW);
+            else
+                TA_WAIT_VMCNT(0);
+        }
         __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): its LDS reads of step j-1 are done
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();           // ... and every other wave's too
         asm volatile("" ::: "memory");          // no LDS access moves across it
-        if (j + 1 < n_steps) {
-            // the other stage was last read in step j-1, which every wave has left
-            issue_dma(j + 1, StageTag<1 - decltype(stage)::value>(), StageTag<0>());
-            prefetch_pages(j + 2);
+        if (j + NSTG - 1 < n_steps) {
+            // that stage was last read in step j-1, which every wave has left
+            issue_dma(j + NSTG - 1, StageTag<(decltype(stage)::value + NSTG - 1) % NSTG>(), StageTag<0>());
+            prefetch_pages(j + NSTG);
         }
         const int k = j * KSB + my_blk;
         if (k < n_blocks) {
             bool is_tree;
             const int start = block_start(k, is_tree);
-            const char *kst = (decltype(stage)::value == 0 ? k_st0 : k_st1) + my_blk * LY::BLK;
-            const char *vst = (decltype(stage)::value == 0 ? v_st0 : v_st1) + my_blk * LY::BLK;
+            const char *kst = kv_lds + 2 * decltype(stage)::value * SBYTES + my_blk * LY::BLK;
+            const char *vst = kst + SBYTES;
 
             // which 32-key tiles of the block this wave computes
             int ktile[NT];
@@ -1109,10 +1128,28 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
         issue_dma(0, StageTag<0>(), StageTag<0>());
         prefetch_pages(1);
     }
-    for (int j = 0; j < n_steps; j += 2) {
+    if constexpr (NSTG == 4) {
+        // steps 1 and 2 go out before the loop, each with the page ids
+        // prefetched just before it
+        if (1 < n_steps) {
+            issue_dma(1, StageTag<1>(), StageTag<0>());
+            prefetch_pages(2);
+        }
+        if (2 < n_steps) {
+            issue_dma(2, StageTag<2>(), StageTag<0>());
+            prefetch_pages(3);
+        }
+    }
+    for (int j = 0; j < n_steps; j += NSTG) {
         step(j, StageTag<0>());
         if (j + 1 < n_steps)
             step(j + 1, StageTag<1>());
+        if constexpr (NSTG == 4) {
+            if (j + 2 < n_steps)
+                step(j + 2, StageTag<2>());
+            if (j + 3 < n_steps)
+                step(j + 3, StageTag<3>());
+        }
     }
     if (KS > 1) {
         // the slice combine below reuses the stages: every wave must be done
@@ -1133,7 +1170,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
         // are free after the barrier above.
         float *xo = (float *)kv_lds;   // [NR][KS][NDT - NDT/KS][32 x 32] fp32, lane-major
         constexpr int NX = NDT - NDT / KS;
-        static_assert(NR * KS * NX * 4096 <= 4 * SBYTES, "combine buffer exceeds the stages");
+        static_assert(NR * KS * NX * 4096 <= 2 * NSTG * SBYTES, "combine buffer exceeds the stages");
         if (hh == 0)
             ml_x[(rtw * KS + ks) * 32 + lr] = float2{m_run, l_tot};
         int x = 0;
@@ -1489,17 +1526,17 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p)
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int D, int NR, int KS>
+template <int D, int NR, int KS, int NSTG = 2>
 static void launch_fwd_bf16_t(const FwdParams &p, hipStream_t stream)
 {
     const dim3 grid(p.units_per_xcd * 8), block(NR * KS * 64);
     if (p.page_shift >= 4)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, NR, KS, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NR, KS, true, NSTG>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, NR, KS, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NR, KS, false, NSTG>), grid, block, 0, stream, p);
 }
 
-hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nr, int ks, hipStream_t stream)
+hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nr, int ks, int nstg, hipStream_t stream)
 {
     if (dtype_fp32) {
         const dim3 row_grid((p.max_tree * p.Hq + 3) / 4, p.B);
@@ -1509,8 +1546,10 @@ hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nr, int ks, hipStr
             hipLaunchKernelGGL((fwd_f32_kernel<128>), row_grid, dim3(256), 0, stream, p);
         return hipGetLastError();
     }
-    // (row tiles, key slices) pairs chosen by the host; anything else is a
+    // (row tiles, key slices, stages) chosen by the host; anything else is a
     // host bug and fails the launch
+    if (nstg != 2 && !(nstg == 4 && p.D == 128 && nr == 8 && ks == 1))
+        return hipErrorInvalidValue;
     if (p.D == 64) {
         if (nr == 1 && ks == 2) launch_fwd_bf16_t<64, 1, 2>(p, stream);
         else if (nr == 2 && ks == 2) launch_fwd_bf16_t<64, 2, 2>(p, stream);
@@ -1522,6 +1561,7 @@ hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nr, int ks, hipStr
         else if (nr == 2 && ks == 2) launch_fwd_bf16_t<128, 2, 2>(p, stream);
         else if (nr == 4 && ks == 2) launch_fwd_bf16_t<128, 4, 2>(p, stream);
         else if (nr == 4 && ks == 1) launch_fwd_bf16_t<128, 4, 1>(p, stream);
+        else if (nr == 8 && ks == 1 && nstg == 4) launch_fwd_bf16_t<128, 8, 1, 4>(p, stream);
         else if (nr == 8 && ks == 1) launch_fwd_bf16_t<128, 8, 1>(p, stream);
         else return hipErrorInvalidValue;
     }

@@ -17,6 +17,9 @@ constexpr int64_t kNumCUs = 256;
 constexpr int64_t kWavesPerCU = 8;
 // (request, kv head, 128-row tile) units from which 4-wave workgroups pay
 constexpr int64_t kWideUnits = 128;
+// prefix length from which the 8-wave workgroups' units are long enough for
+// copies issued three steps ahead (four K/V stages) to pay
+constexpr int64_t kDeepPrefix = 1024;
 
 bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -50,7 +53,8 @@ int32_t waves_for(int32_t rows)
 
 struct Geometry {
     int32_t nr, ks, n_rt, nsplit, chunk;
-    bool tree_slot;   // nsplit > 1: the last slot runs the tree alone
+    int32_t nstg = 2;   // K/V stages in LDS (4: copies three steps ahead)
+    bool tree_slot;     // nsplit > 1: the last slot runs the tree alone
 };
 
 // key slices per row tile (waves of one row tile that split each step's
@@ -94,14 +98,25 @@ Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tre
     const int32_t rows = max_tree * G;
     g.nr = waves_for(rows);
     g.ks = slices_for(g.nr, D);
-    // With plenty of work units, head_dim 128 runs 4-wave workgroups (4 row
-    // tiles, one slice) instead of 8-wave ones: two fit on a CU, and as
-    // independent workgroups (no shared barrier) one's softmax overlaps the
-    // other's MFMAs (measured: budget-256 and mixed batches 3-5 % faster; a
-    // single request, with few units, is not)
-    if (D == 128 && g.nr == 8 && (int64_t)B * Hkv * ceil_div(rows, 128) >= kWideUnits) {
-        g.nr = 4;
-        g.ks = 1;
+    // Head_dim 128 with many rows per (request, kv head):
+    // - when the 8-wave workgroups (256 rows) alone fill the GPU and walk long
+    //   prefixes, they stay, with four K/V stages: copies go out three steps
+    //   ahead (32 requests, budget 256, 4096-token prefixes: attention kernel
+    //   579 -> 563 us; with 5-block units, as for a single request of budget
+    //   256, the deeper prologue costs 2 %, so shorter prefixes keep two);
+    // - else, with plenty of work units, 4-wave workgroups (4 row tiles, one
+    //   slice): two fit on a CU, and as independent workgroups (no shared
+    //   barrier) one's softmax overlaps the other's MFMAs (measured against
+    //   8-wave ones with two stages: budget-256 and mixed batches 3-5 %
+    //   faster; a single request, with few units, is not).
+    if (D == 128 && g.nr == 8) {
+        if ((int64_t)B * Hkv * ceil_div(rows, 256) >= kNumCUs && max_prefix >= kDeepPrefix &&
+            dtype == TA_DTYPE_BF16) {
+            g.nstg = 4;
+        } else if ((int64_t)B * Hkv * ceil_div(rows, 128) >= kWideUnits) {
+            g.nr = 4;
+            g.ks = 1;
+        }
     }
     g.n_rt = rows > 0 ? (int32_t)ceil_div(rows, 32 * g.nr) : 1;
     const int32_t nw = g.nr * g.ks;
@@ -524,7 +539,7 @@ ta_status_t run_fwd(const void *q, const void *k_tree, const void *v_tree, const
     p.plan_status = fp ? fp->status : nullptr;
     hipStream_t s = (hipStream_t)stream;
     if (stages & kStagePartial) {
-        if (ta::launch_fwd(p, dtype == TA_DTYPE_FP32, g.nr, g.ks, s) != hipSuccess)
+        if (ta::launch_fwd(p, dtype == TA_DTYPE_FP32, g.nr, g.ks, g.nstg, s) != hipSuccess)
             return TA_ERR_HIP;
     }
     if (stages & kStageMerge) {
