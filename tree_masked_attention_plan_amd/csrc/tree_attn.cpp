@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/tree_attn.h: argument checks,
 // the split-K choice, workspace layout and kernel dispatch.  Every check runs
 // before any HIP call so that bad arguments never reach the device.
+#include <algorithm>
 #include <initializer_list>
 #include <math.h>
 #include <stddef.h>
@@ -20,6 +21,9 @@ constexpr int64_t kWideUnits = 128;
 // prefix length from which the 8-wave workgroups' units are long enough for
 // copies issued three steps ahead (four K/V stages) to pay
 constexpr int64_t kDeepPrefix = 1024;
+// longest prefix chunk, in keys, that a single request's 8-wave units are
+// given while the GPU has CUs to spare
+constexpr int64_t kLongChunk = 640;
 
 bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -141,6 +145,16 @@ Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tre
                 target = target * 3 / 2;
             if (base > 0 && base < target)
                 nslot = ceil_div(target, base);
+            if (B <= 1 && g.nr == 8 && D == 128 && base > 0) {
+                // A single request with 8-wave units: each slot beyond the
+                // first costs partial writes and merge reads, so the slots
+                // fill three quarters of the CUs, and long prefixes take
+                // more, up to one workgroup per CU, to keep chunks at most
+                // kLongChunk keys.
+                const int64_t lo = ceil_div(kNumCUs * 3 / 4, base);
+                const int64_t hi = std::min<int64_t>(ceil_div(kNumCUs, base), 1 + ceil_div(max_prefix, kLongChunk));
+                nslot = std::max<int64_t>(1, std::max(lo, hi));
+            }
         }
         if (nslot > ta::kMaxSplits)
             nslot = ta::kMaxSplits;
