@@ -112,7 +112,8 @@ hipError_t launch_build_tree(const TreeParams &p, hipStream_t stream);
 // accepted-path commit: one workgroup per request
 hipError_t launch_commit(const CommitParams &p, hipStream_t stream);
 // nr: 32-row tiles per workgroup of the bf16 kernel; ks: waves per row tile
-// that split each step's keys (see fwd_bf16_kernel)
+// that split each step's keys; nstg: K/V stages in LDS, 2, or 4 for 8 row
+// tiles with one slice at head_dim 128 (see fwd_bf16_kernel)
 hipError_t launch_fwd(const FwdParams &p, int dtype_fp32, int nr, int ks, int nstg, hipStream_t stream);
 // split-K merge of the partials written by launch_fwd (no-op for one split)
 hipError_t launch_merge(const FwdParams &p, hipStream_t stream);
