@@ -307,6 +307,43 @@ def test_random_configurations(dev, i):
     assert_close(w, out, lse, o_ref, l_ref, f"{name} splits={splits}")
 
 
+def test_invisible_tree_keys_get_exact_zero_weight(dev):
+    """A tree node's K and V reach only its own rows and its descendants'
+    (JetFlow technical summary, section 2, the tree-causal mask).  Giving a
+    leaf huge but finite K and V (V = 1e30) must leave every other row's
+    output and LSE bit-identical, with and without splits: inside a computed
+    tile an invisible key's weight is an exact zero.  The leaf's own rows
+    still meet the per-element bar against the oracle (one bf16 step of the
+    exact value, or 1e-2)."""
+    import dataclasses
+    rng = W.rng_for(21, 0)
+    w = small("invisible-huge", [300, 1000], [W.best_first_tree(100, rng), W.best_first_tree(64, rng)],
+              Hq=8, Hkv=2, seed=21)
+    par = w.parent.numpy()[:100]
+    has_child = np.zeros(100, bool)
+    has_child[par[par >= 0]] = True
+    leaves = [j for j in range(100) if not has_child[j] and j % 64 not in (0, 63)]
+    j = leaves[len(leaves) // 2]
+    w2 = dataclasses.replace(w, k_tree=w.k_tree.clone(), v_tree=w.v_tree.clone())
+    w2.k_tree[j] = (w.k_tree[j].float() * 40).to(w.k_tree.dtype)
+    w2.v_tree[j] = torch.full_like(w.v_tree[j], 1e30)
+    others = torch.ones(w.N, dtype=torch.bool)
+    others[j] = False
+    o_ref, l_ref = oracle.tree_attn_workload(w2)
+    o_ref = torch.as_tensor(o_ref).reshape(w.N, w.Hq, w.D).double()
+    l_ref = torch.as_tensor(l_ref).reshape(w.N, w.Hq).double()
+    for ns in (0, 1, 5):
+        o1, l1 = gpu_fwd(w, dev, num_splits=ns)
+        o2, l2 = gpu_fwd(w2, dev, num_splits=ns)
+        say(f"  leaf {j}: splits {ns}, leaf rows max |O| {o2[j].abs().max():.3e}")
+        assert torch.equal(o1[others], o2[others]) and torch.equal(l1[others], l2[others]), \
+            f"splits={ns}: rows that cannot see node {j} changed"
+        assert torch.isfinite(o2[j]).all()
+        eo = (o2[j] - bf16_round(o_ref[j])).abs()
+        assert (eo <= torch.clamp(bf16_ulp(o_ref[j]), min=1e-2)).all(), f"splits={ns}: leaf rows {eo.max()}"
+        assert (l2[j] - l_ref[j]).abs().max() <= 1e-2, f"splits={ns}: leaf lse"
+
+
 def test_softmax_scale_override(dev):
     rng = W.rng_for(8, 0)
     w = small("scale", [90], [W.best_first_tree(30, rng)], seed=8)
