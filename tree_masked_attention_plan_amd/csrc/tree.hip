@@ -162,6 +162,126 @@ __device__ __forceinline__ void rank_children(const uint64_t *ckey, int32_t *cpo
     }
 }
 
+// The same positions for many children, E = 2, 4 or 8 per thread (m <=
+// 256 E): the children's ranks among themselves come from a bitonic sort of
+// their keys, best first, instead of counting all pairs.  Thread tid holds
+// positions tid*E .. tid*E+E-1; positions from m on are padding (key 0,
+// below every child).  At distance j an exchange stays inside a thread for
+// j < E, goes between the lanes of a wave (shuffles) for j < 64 E, and
+// through LDS (xk: M keys, xi: M indices; xk may be ckey itself, read
+// before the first exchange) beyond.  The sort costs log2(M)(log2(M)+1)/2
+// short stages where the count costs m/256 compares of every key per thread.
+template <int E>
+__device__ __forceinline__ void rank_children_sorted(const uint64_t *ckey, int32_t *cpos, int32_t *hist,
+                                                     uint64_t *xk, int32_t *xi, const uint64_t *lkey, int n,
+                                                     int m, int tid)
+{
+    constexpr int M = 256 * E;
+    uint64_t k[E];
+    int ix[E], lo[E], hi[E];
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const int c = tid * E + r;
+        k[r] = c < m ? ckey[c] : 0ull;
+        ix[r] = c;
+        lo[r] = 0;
+        hi[r] = c < m ? n : 0;
+    }
+    // kept nodes above each child: binary searches, interleaved
+    for (int round = 0; round < 9; ++round) {
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+            if (lo[r] < hi[r]) {
+                const int mid = (lo[r] + hi[r]) >> 1;
+                if (lkey[mid] > k[r])
+                    lo[r] = mid + 1;
+                else
+                    hi[r] = mid;
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const int c = tid * E + r;
+        if (c < m) {
+            cpos[c] = lo[r];
+            if (lo[r] < n)
+                atomicAdd(&hist[lo[r]], 1);
+        }
+    }
+    // children above each child: bitonic sort, descending
+    for (int size = 2; size <= M; size <<= 1) {
+        for (int j = size >> 1; j > 0; j >>= 1) {   // j and size are uniform
+            if (j < E) {
+#pragma unroll
+                for (int jj = 1; jj < E; jj <<= 1) {
+                    if (j != jj)
+                        continue;
+#pragma unroll
+                    for (int r = 0; r < E; ++r) {
+                        const int pr = r ^ jj;
+                        if (pr <= r)
+                            continue;   // each pair once, from its lower position
+                        const bool desc = ((tid * E + r) & size) == 0;
+                        if (desc ? (k[r] < k[pr]) : (k[r] > k[pr])) {
+                            const uint64_t tk = k[r];
+                            k[r] = k[pr];
+                            k[pr] = tk;
+                            const int ti = ix[r];
+                            ix[r] = ix[pr];
+                            ix[pr] = ti;
+                        }
+                    }
+                }
+                continue;
+            }
+            uint64_t ok[E];
+            int oi[E];
+            if (j < 64 * E) {
+                const int lj = j / E;   // the partner's lane distance, same wave
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    const uint32_t h = (uint32_t)__shfl_xor((int)(uint32_t)(k[r] >> 32), lj);
+                    const uint32_t l = (uint32_t)__shfl_xor((int)(uint32_t)k[r], lj);
+                    ok[r] = ((uint64_t)h << 32) | l;
+                    oi[r] = __shfl_xor(ix[r], lj);
+                }
+            } else {
+                __syncthreads();   // the previous readers of xk / xi are done
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    xk[tid * E + r] = k[r];
+                    xi[tid * E + r] = ix[r];
+                }
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    const int q = (tid * E + r) ^ j;
+                    ok[r] = xk[q];
+                    oi[r] = xi[q];
+                }
+            }
+            // the lower position of a pair keeps the better key in a
+            // descending run and the worse in an ascending one
+#pragma unroll
+            for (int r = 0; r < E; ++r) {
+                const int i = tid * E + r;
+                const bool lower = (i & j) == 0;
+                const bool desc = (i & size) == 0;
+                if ((lower == desc) ? (ok[r] > k[r]) : (ok[r] < k[r])) {
+                    k[r] = ok[r];
+                    ix[r] = oi[r];
+                }
+            }
+        }
+    }
+    __syncthreads();   // every child's kept-node count is in cpos
+#pragma unroll
+    for (int r = 0; r < E; ++r)
+        if (ix[r] < m)
+            cpos[ix[r]] += tid * E + r;
+}
+
 __global__ __launch_bounds__(256) void build_tree_kernel(TreeParams p)
 {
     constexpr int NT = 256;
@@ -178,6 +298,7 @@ __global__ __launch_bounds__(256) void build_tree_kernel(TreeParams p)
     __shared__ float csc[CH];
     __shared__ int32_t cinfo[CH];   // (parent position + 1) << 8 | token
     __shared__ int32_t cpos[CH];
+    __shared__ int32_t sidx[CH];    // sort scratch: child indices
     // the kept depth-d nodes at the start of depth d: score, and where each
     // is now (-1 once dropped)
     __shared__ float par_sc[kMaxTree];
@@ -276,6 +397,12 @@ __global__ __launch_bounds__(256) void build_tree_kernel(TreeParams p)
             // new positions: kept nodes above a child (binary search in the
             // sorted list) plus new children above it
             const int cpt = (m + NT - 1) / NT;   // children per thread (uniform)
+            // up to 1024 children: count all pairs; more: sort (its 45, 55
+            // or 66 dependent stages for 512, 1024 or 2048 positions cost
+            // more than the count below that:
+            // 32 requests, budget 256, 8 candidates: 72 us counting, 79
+            // sorting from 513 children, 87 from 257; 8 requests with 64
+            // candidates: 148 -> 130 us sorting from 1025)
             if (cpt == 1)
                 rank_children<1>(ckey, cpos, hist, lkey[buf], n, m, tid);
             else if (cpt == 2)
@@ -283,7 +410,7 @@ __global__ __launch_bounds__(256) void build_tree_kernel(TreeParams p)
             else if (cpt <= 4)
                 rank_children<4>(ckey, cpos, hist, lkey[buf], n, m, tid);
             else
-                rank_children<CH / NT>(ckey, cpos, hist, lkey[buf], n, m, tid);
+                rank_children_sorted<CH / NT>(ckey, cpos, hist, ckey, sidx, lkey[buf], n, m, tid);
             __syncthreads();
             // a kept node at position i moves down by the children above it,
             // those whose binary-search position is <= i
