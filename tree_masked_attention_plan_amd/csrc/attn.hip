@@ -1237,6 +1237,71 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     const float lse2 = l_tot > 0.f ? m_fin + __builtin_log2f(l_tot) : -INFINITY;
     const int64_t n = R.off + node;
     const bool lse_writer = hh == 0 && ks == 0;
+    if (KS == 1 && NSTG == 2 && p.nsplit > 1) {
+        // One slice, split partials: the rows go out through LDS.  A lane
+        // holds 8 bytes of each 16-byte chunk of its row, so storing from
+        // registers writes 16 bytes into each of 32 rows per instruction,
+        // and the L2 sees 16-byte requests.  Each wave instead stages its 32
+        // rows in a region of its own (row-major, chunks XOR-swizzled by
+        // row) and stores whole rows, D/8 lanes per row.  The values are
+        // converted exactly as below, so the results are the same bits
+        // (budget 256, one request: step 27.4 -> 26.6 us; 8 requests of
+        // budget 64: 46.1 -> 45.6 us).  Unsplit outputs keep the direct
+        // stores: there the barrier and the round trip cost more (32
+        // requests of budget 256: 554 -> 568 us when staged), and the
+        // four-stage form, which serves that shape, does not hold this
+        // code at all (with it, unused, it ran 556 -> 579 us).
+        static_assert(NW * 32 * LY::ROWB <= 2 * NSTG * SBYTES, "output staging exceeds the stages");
+        constexpr int CPR = LY::CPR;      // 16-byte chunks per row
+        constexpr int RPS = 64 / CPR;     // rows per store instruction
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();     // every wave has left the last step: the stages are free
+        asm volatile("" ::: "memory");
+        // the partial row scaled by 2^-e (see below)
+        float am = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                am = fmaxf(am, __builtin_fabsf(acc_o[dt][i]));
+        am = fmaxf(am, __shfl_xor(am, 32));
+        const float mo = am * inv;
+        const int ex = mo > 0.f ? __builtin_amdgcn_frexp_expf(mo) - 15 : 0;
+        char *const wreg = kv_lds + wv * (32 * LY::ROWB);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                f16x4 v;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    v[j] = (_Float16)__builtin_ldexpf(acc_o[dt][i4 * 4 + j] * inv, -ex);
+                const u32x2 w2 = __builtin_bit_cast(u32x2, v);
+                const int q = dt * 4 + i4;   // the chunk of columns dt*32 + i4*8 .. +8
+                *(u32x2 *)(wreg + lr * LY::ROWB + ((q ^ (lr & (CPR - 1))) * 16) + hh * 8) = w2;
+            }
+        }
+        if (lse_writer && row_ok)
+            gmem((f32x2 *)p.ws_ml)[((int64_t)u.s * p.N + n) * p.Hq + qh] = f32x2{lse2, (float)ex};
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 32 / RPS; ++i) {
+            const int rr = i * RPS + lane / CPR;
+            const int q = lane % CPR;
+            const u32x4 v = *(const u32x4 *)(wreg + rr * LY::ROWB + ((q ^ (rr & (CPR - 1))) * 16));
+            const int mr = row0 + rtw * 32 + rr;   // the row's index among the (b, c) rows
+            if (mr < rows) {
+                const int nd = mr / p.G;
+                const int64_t nn = R.off + nd;
+                const int qr = c * p.G + (mr - nd * p.G);
+                uint16_t *dst = p.ws_o + (((int64_t)u.s * p.N + nn) * p.Hq + qr) * D;
+                *(__attribute__((address_space(1))) u32x4 *)(gmem(dst) + q * 8) = v;
+            }
+        }
+        return;
+    }
     if (p.nsplit == 1) {
         if (!row_ok)
             return;
