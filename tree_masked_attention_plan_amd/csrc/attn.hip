@@ -727,8 +727,24 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
         }
     };
 
-    // The split's first prefix step is copied before Q and the mask words
-    // are loaded, so the three travel together.
+    // Q^T fragments (B operand): lane holds Q[row][kc*16 + hh*8 .. +8].
+    // Issued first: a wave's copy instructions below take about 116 clocks
+    // each to issue, and behind them the Q loads went out late (budget 16,
+    // one request: attention kernel 9.32 -> 9.03 us with Q first).
+    bf16x8 qf[NKC];
+    {
+        const auto qrow = gmem((const uint16_t *)p.q + ((int64_t)(R.off + node) * p.Hq + qh) * D);
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row_ok)
+                v = *(const __attribute__((address_space(1))) u32x4 *)(qrow + kc * 16 + hh * 8);
+            qf[kc] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    // The split's first prefix step is copied right after the Q loads and
+    // before the mask words are loaded, so the three travel together.
     // (a unit that owns the tree copies early only a step of prefix blocks:
     // which tree blocks it needs is known after the mask words arrive)
     const bool early = SP && n_pre > 0 && (n_pre >= KSB || !R.owns_tree);
@@ -746,19 +762,6 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
     if (early_tree) {
         tree_need = 1;
         issue_dma(0, StageTag<0>(), StageTag<0>());
-    }
-
-    // Q^T fragments (B operand): lane holds Q[row][kc*16 + hh*8 .. +8]
-    bf16x8 qf[NKC];
-    {
-        const auto qrow = gmem((const uint16_t *)p.q + ((int64_t)(R.off + node) * p.Hq + qh) * D);
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row_ok)
-                v = *(const __attribute__((address_space(1))) u32x4 *)(qrow + kc * 16 + hh * 8);
-            qf[kc] = __builtin_bit_cast(bf16x8, v);
-        }
     }
 
     // tree blocks this workgroup needs (only the unit that owns the tree)
