@@ -34,6 +34,38 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Stores of split partials (rows and (lse, exponent) pairs) with the
+// agent-scope bit set: the lines are written through the XCD's L2 instead of
+// staying dirty there.  The kernel's end then has no partials to write back
+// from the L2s, and the merge kernel, whose rows sit on other XCDs anyway,
+// reads them from memory as before.  Same bits; one request of budget 16:
+// step 12.22 -> 11.96 us; budget 256: 26.58 -> 25.11 us; 8 requests of
+// budget 64: 45.8 -> 44.4 us.  The merge's and the unsplit outputs keep plain
+// stores: written through, the merge step slowed 0.4 us and 32 requests of
+// budget 256 went 563 -> 586 us; the non-temporal hint instead slowed the
+// merge (its reads of such partials) and that batch (641 us).
+// Nothing in the kernels loads from global memory after these stores, so
+// that the compiler's wait counts, which do not see them, stay exact; a
+// 16-byte store needs one wait state before its data registers are written
+// again, which the trailing s_nop gives (the hazard check does not look
+// inside asm).
+template <class P>
+__device__ __forceinline__ void store_through(P ptr, u32x4 v)
+{
+    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 0"
+                 :
+                 : "v"((uint64_t)(uintptr_t)ptr), "v"(v)
+                 : "memory");
+}
+template <class P>
+__device__ __forceinline__ void store_through(P ptr, u32x2 v)
+{
+    asm volatile("global_store_dwordx2 %0, %1, off sc1"
+                 :
+                 : "v"((uint64_t)(uintptr_t)ptr), "v"(v)
+                 : "memory");
+}
+
 static constexpr float kLn2 = 0.69314718055994530942f;
 // Rescale the running output only when a row's max grows by more than this
 // (in log2 units).  Probabilities then stay below 2^8, far inside fp32 and
@@ -518,7 +550,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
         // partial lse is -inf, so the merge gives it zero weight and never
         // reads its partial output
         if (row_ok && hh == 0 && ks == 0)
-            gmem((f32x2 *)p.ws_ml)[((int64_t)u.s * p.N + R.off + node) * p.Hq + qh] = f32x2{-INFINITY, 0.f};
+            store_through(&gmem((f32x2 *)p.ws_ml)[((int64_t)u.s * p.N + R.off + node) * p.Hq + qh], __builtin_bit_cast(u32x2, f32x2{-INFINITY, 0.f}));
         return;   // uniform across the workgroup
     }
     const int c = u.c;
@@ -1286,7 +1318,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
             }
         }
         if (lse_writer && row_ok)
-            gmem((f32x2 *)p.ws_ml)[((int64_t)u.s * p.N + n) * p.Hq + qh] = f32x2{lse2, (float)ex};
+            store_through(&gmem((f32x2 *)p.ws_ml)[((int64_t)u.s * p.N + n) * p.Hq + qh], __builtin_bit_cast(u32x2, f32x2{lse2, (float)ex}));
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
         asm volatile("" ::: "memory");
 #pragma unroll
@@ -1300,7 +1332,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
                 const int64_t nn = R.off + nd;
                 const int qr = c * p.G + (mr - nd * p.G);
                 uint16_t *dst = p.ws_o + (((int64_t)u.s * p.N + nn) * p.Hq + qr) * D;
-                *(__attribute__((address_space(1))) u32x4 *)(gmem(dst) + q * 8) = v;
+                store_through(gmem(dst) + q * 8, v);
             }
         }
         return;
@@ -1385,7 +1417,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
             }
         }
         if (lse_writer && row_ok)
-            gmem((f32x2 *)p.ws_ml)[((int64_t)u.s * p.N + n) * p.Hq + qh] = f32x2{lse2, (float)ex};
+            store_through(&gmem((f32x2 *)p.ws_ml)[((int64_t)u.s * p.N + n) * p.Hq + qh], __builtin_bit_cast(u32x2, f32x2{lse2, (float)ex}));
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
         asm volatile("" ::: "memory");
         constexpr int RPS = 64 / CPW;          // rows per store instruction
@@ -1400,7 +1432,7 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
                 const int64_t nn = R.off + nd;
                 const int qr = c * p.G + (mr - nd * p.G);
                 const int col = (ks + KS * (lq >> 2)) * 32 + (lq & 3) * 8;
-                *(__attribute__((address_space(1))) u32x4 *)(gmem(p.ws_o + (((int64_t)u.s * p.N + nn) * p.Hq + qr) * D) + col) = v;
+                store_through(gmem(p.ws_o + (((int64_t)u.s * p.N + nn) * p.Hq + qr) * D) + col, v);
             }
         }
         return;
@@ -1417,11 +1449,11 @@ __global__ __launch_bounds__(NR * KS * 64) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     v[j] = (_Float16)__builtin_ldexpf(acc_o[dt][i4 * 4 + j] * inv, -ex);
-                *(__attribute__((address_space(1))) f16x4 *)(orow + dt * 32 + i4 * 8 + hh * 4) = v;
+                store_through(orow + dt * 32 + i4 * 8 + hh * 4, __builtin_bit_cast(u32x2, v));
             }
         }
         if (lse_writer)
-            gmem((f32x2 *)p.ws_ml)[((int64_t)u.s * p.N + n) * p.Hq + qh] = f32x2{lse2, (float)ex};
+            store_through(&gmem((f32x2 *)p.ws_ml)[((int64_t)u.s * p.N + n) * p.Hq + qh], __builtin_bit_cast(u32x2, f32x2{lse2, (float)ex}));
     }
 }
 
