@@ -206,6 +206,7 @@ def test_split_choice_for_the_named_workloads():
     assert ta.num_splits(1, 4, 1, 64, 16, 128, __import__("torch").float32) == 1    # tiny (fp32)
     assert ta.num_splits(1, 32, 8, 128, 16, 2048) == 17                                # chain16
     assert ta.num_splits(1, 32, 8, 128, 256, 2048) == 6                                # tree256
+    assert ta.num_splits(1, 32, 8, 128, 256, 8192) == 8    # one request, long prefix: no tree slot
     assert ta.num_splits(8, 32, 8, 128, 64, 8192) == 5                                 # mixed
     assert ta.num_splits(32, 32, 4, 128, 256, 4096) == 1                               # moe
 

@@ -207,6 +207,10 @@ def small_cases():
          [W.best_first_tree(int(t), rng) for t in rng.integers(129, 257, 32)], dict(Hq=8, Hkv=8, ps=8)),
         ("four-stages-page256", [int(x) for x in rng.integers(900, 1300, 32)],
          [W.random_tree(int(t), 12, rng) for t in rng.integers(129, 180, 32)], dict(Hq=8, Hkv=8, ps=256)),
+        # one request of 8-wave units with a prefix of at least 4096 keys: the
+        # tree rides with the last prefix chunk (8 keys of prefix, then the
+        # tree's two blocks) instead of taking a slot of its own
+        ("tree-rides-long-prefix", [5000], [W.best_first_tree(100, rng)], {}),
     ]
     return cases
 

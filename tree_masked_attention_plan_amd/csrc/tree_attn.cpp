@@ -24,6 +24,9 @@ constexpr int64_t kDeepPrefix = 1024;
 // longest prefix chunk, in keys, that a single request's 8-wave units are
 // given while the GPU has CUs to spare
 constexpr int64_t kLongChunk = 640;
+// prefix length from which a single request's tree rides with its last prefix
+// chunk instead of taking a slot of its own
+constexpr int64_t kTreeRidesPrefix = 4096;
 
 bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -176,6 +179,23 @@ Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tre
         npre = ceil_div(max_prefix, chunk);
         g.nsplit = (int32_t)(g.tree_slot ? npre + 1 : npre);
         g.chunk = (int32_t)chunk;
+        if (g.tree_slot && forced_splits <= 0 && g.nr == 8 && step_keys == ta::kBlockKeys &&
+            max_prefix >= kTreeRidesPrefix) {
+            // A single request with a long prefix: the tree rides with the
+            // last prefix chunk, and the chunks are cut so that this one's
+            // prefix blocks plus the tree's match the others.  Graph replay,
+            // budget 200-256 trees: 4096-token prefix 30.1 -> 29.6 us, 6000
+            // 37.2 -> 35.8 us, 8192 46.2 -> 44.8 us.  Shorter prefixes keep
+            // the tree slot: the tree phase (masks, and the plan when it is
+            // built in the same call) costs more than its block count, and
+            // riding lost 1-28 % there (2048: 24.2 -> 24.7 us).
+            const int64_t pb = ceil_div(max_prefix, ta::kBlockKeys);
+            const int64_t tb = ceil_div(max_tree, ta::kBlockKeys);
+            const int64_t cb = std::max<int64_t>(1, ceil_div(pb + tb, g.nsplit));
+            g.tree_slot = false;
+            g.chunk = (int32_t)(cb * ta::kBlockKeys);
+            g.nsplit = (int32_t)ceil_div(max_prefix, (int64_t)g.chunk);
+        }
     }
     return g;
 }
