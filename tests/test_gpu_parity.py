@@ -481,6 +481,37 @@ def test_partial_then_merge_equals_fwd(dev):
         assert torch.equal(o1, call.out) and torch.equal(l1, call.lse)
 
 
+def test_one_workspace_across_split_counts(dev):
+    """One caller-owned workspace, filled with NaN bytes (fp16 and fp32) before
+    the first call, serves calls whose split counts and shapes go down and up
+    again.  Slots a call does not write keep what an earlier call, or the
+    fill, left there; the merge must read only what the current call wrote
+    (partial rows of zero-weight slots are excluded by a select, not a
+    multiplication)."""
+    rng = W.rng_for(33, 0)
+    wa = small("ws-a", [900, 300, 0], [W.best_first_tree(40, rng), W.chain(7), W.chain(3)], seed=33)
+    wb = small("ws-b", [250], [W.random_tree(30, 5, rng)], seed=34)
+    refs = {w.name: oracle.tree_attn_workload(w) for w in (wa, wb)}
+    dws = {w.name: w.to(dev) for w in (wa, wb)}
+    plans = {}
+    for w in (wa, wb):
+        wd = dws[w.name]
+        plans[w.name] = ta.plan(wd.parent, wd.tree_off, wd.prefix_len, max_tree=w.max_tree).anc_mask
+    need = max(ta.workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.max_tree, w.max_prefix, num_splits=ns)
+               for w in (wa, wb) for ns in (3, 5, 12))
+    ws = torch.full((need + 256,), 0xFF, dtype=torch.uint8, device=dev)
+    for w, ns in ((wa, 12), (wb, 3), (wa, 5), (wb, 12), (wa, 3)):
+        say(f"shared workspace: {w.name} splits={ns}")
+        wd = dws[w.name]
+        out, lse = ta.fwd(wd.q, wd.k_tree, wd.v_tree, wd.k_cache, wd.v_cache, wd.block_table,
+                          wd.prefix_len, wd.tree_off, plans[w.name], max_tree=w.max_tree,
+                          max_prefix=w.max_prefix, num_splits=ns, workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, l_ref = refs[w.name]
+        assert_close(w, out.float().cpu().double(), lse.cpu().double(), o_ref, l_ref,
+                     f"{w.name} splits={ns}, shared workspace")
+
+
 def test_empty_batch_is_noop(dev):
     say("empty batch")
     e = torch.zeros(0, dtype=torch.int32, device=dev)
