@@ -13,7 +13,9 @@ working set does not stay in the 256 MB Infinity Cache.  Before any timing,
 at least 1.5 s of untimed steps bring the clocks up (and keep the GPU
 visibly busy to an outside utilisation sampler), whatever ``--warmup`` says; then ``--warmup`` untimed steps, then exactly ``--steps`` steps timed
 with HIP events on the replay stream.  ``value`` is tree tokens per second of
-that GPU time.
+that GPU time.  The headline workload then runs on, back to back, for
+``--sustain-seconds`` of GPU time (default 8), reported as ``sustained``: the
+rate over that run and its slowest half-second block.
 
 Beside it: ``fwd_only`` (tree_attn_fwd alone, mask words from an earlier
 plan), ``plan_only`` (tree_attn_plan alone), ``two_call`` (plan, then
@@ -281,6 +283,39 @@ def time_steps(runner: Runner, steps: int, warmup: int) -> tuple:
     return e0.elapsed_time(e1) / 1e3, wall
 
 
+def sustain(runner: Runner, seconds: float, tree_tokens: int) -> dict:
+    """Whole replica cycles back to back for about ``seconds`` of GPU time,
+    after the timed steps: whether the step rate holds over a long run, with
+    clocks and power at steady state.  Timed with HIP events on the replay
+    stream around blocks of about half a second; reports the rate over all
+    blocks and the slowest block's."""
+    R = len(runner.reps)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    runner.chunk.replay()
+    e1.record(stream)
+    e1.synchronize()
+    per_cycle = max(e0.elapsed_time(e1) / 1e3, 1e-6)
+    n = max(1, int(0.5 / per_cycle))                            # cycles per block
+    blocks = max(1, int(round(seconds / (n * per_cycle))))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
+    _busy_stream(runner)
+    ev[0].record(stream)
+    for i in range(blocks):
+        for _ in range(n):
+            runner.chunk.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    times = [ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(blocks)]
+    steps = blocks * n * R
+    total = sum(times)
+    return {"seconds": total, "steps": steps, "blocks": blocks,
+            "value": tree_tokens * steps / total, "ms_per_step": total / steps * 1e3,
+            "slowest_block_value": tree_tokens * n * R / max(times)}
+
+
 def time_partial_kernel(runner: Runner, min_launches: int = 200, graph=None) -> float:
     """Average duration (s) of one attention-kernel launch (or, with
     ``graph``, of one call of what it captured per replica): HIP events on
@@ -386,10 +421,12 @@ BOUND = {"tiny": "hbm", "chain16": "hbm", "tree256": "mfma", "mixed": "mfma", "m
 
 
 def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: float,
-            compare: bool = True) -> dict:
+            compare: bool = True, sustain_s: float = 0.0) -> dict:
     """One workload: ``warmup`` untimed steps after a clock ramp, then
     exactly ``steps`` steps timed with HIP events on the replay stream.
-    ``value`` = tree tokens per second of GPU time over those steps."""
+    ``value`` = tree tokens per second of GPU time over those steps.  With
+    ``sustain_s`` > 0 the steps then run on for about that many seconds
+    (:func:`sustain`)."""
     w = W.make_config(name)
     per = replica_bytes(w)
     R = max(1, min(MAX_REPLICAS, math.ceil(ROTATE_BYTES / per)))
@@ -443,6 +480,10 @@ def measure(name: str, steps: int, warmup: int, dev, cpu: bool, cpu_seconds: flo
     res["roofline"] = roofline(BOUND[name], wk, t_kern, name, kernel, peak)
     if name == "mixed":
         res["roofline_hbm"] = roofline("hbm", wk, t_kern, name, kernel, peak)
+    if sustain_s > 0:
+        res["sustained"] = sustain(runner, sustain_s, wk["tree_tokens"])
+        log(f"[bench] {name}: sustained {res['sustained']['ms_per_step'] * 1e3:.2f} us/step over "
+            f"{res['sustained']['seconds']:.1f} s of GPU time ({res['sustained']['steps']} steps)")
     del runner, reps
     torch.cuda.empty_cache()
     if cpu:
@@ -662,6 +703,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the two-call, plan-only and forward-only timings (profiling runs)")
+    ap.add_argument("--sustain-seconds", type=float, default=8.0,
+                    help="GPU seconds of back-to-back steps after the timed ones, reported as "
+                         "'sustained' (0: none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget of the headline workload (the others get half)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -694,7 +738,8 @@ def main():
     dev = torch.device("cuda:0")
     cpu = not args.no_cpu_baseline
     compare = not args.no_compare
-    main_res = measure(args.workload, args.steps, args.warmup, dev, cpu, args.cpu_seconds, compare)
+    main_res = measure(args.workload, args.steps, args.warmup, dev, cpu, args.cpu_seconds, compare,
+                       args.sustain_seconds)
     w_dtype = "f32" if args.workload == "tiny" else "bf16"
     line = {
         "metric": METRIC,
@@ -719,6 +764,8 @@ def main():
                                 "merge), timed with HIP events on the replay stream")
     for k in ("wall_ms_per_step", "tflops", "kernel_us", "fwd_only", "plan_only", "two_call"):
         line[k] = main_res[k]
+    if "sustained" in main_res:
+        line["sustained"] = main_res["sustained"]
     if not args.no_secondary:
         # steps per workload: about the same GPU time as the headline's at
         # the default --steps; at least 20
