@@ -143,9 +143,14 @@ Geometry geometry(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_tre
             // chunks are cut to the longest: finer chunks keep the long
             // requests' units from trailing the rest (8 requests of 512 to
             // 4051 keys, budget 64: 5 prefix chunks, attention kernel 39.9 us,
-            // against 3 chunks 52.5 us and 7 chunks 46.3 us)
+            // against 3 chunks 52.5 us and 7 chunks 46.3 us); batches of the
+            // 4-wave budget-16 shape take twice the target (one-call step,
+            // against 1.5 times: 16 requests 42.7 -> 40.0 us, 8 requests of
+            // 2048 keys 21.2 -> 19.9 us, 12 requests 33.8 -> 27.9 us; over
+            // ten such batch shapes the count is within 3 % of the best
+            // forced count on eight)
             if (B > 1)
-                target = target * 3 / 2;
+                target = (g.nr == 2 && D == 128) ? target * 2 : target * 3 / 2;
             if (base > 0 && base < target)
                 nslot = ceil_div(target, base);
             if (B <= 1 && g.nr == 8 && D == 128 && base > 0) {
